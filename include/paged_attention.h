@@ -1,0 +1,160 @@
+/*
+ * paged_attention.h -- C ABI of the MI355X (gfx950) paged decode library (libpa.so).
+ *
+ * Two operations on a KV cache held as fixed-size physical blocks in one pool,
+ * reached through per-sequence block tables:
+ *
+ *   pa_write_kv  -- the slot write: each new token's K and V go into its slot
+ *                   of the sequence's current block.  Defined by "How does vLLM
+ *                   PagedAttention manage Virtual Memory Pages to eliminate KV
+ *                   cache fragmentation?", sections "Key Technical Innovations"
+ *                   (item 2: blocks of e.g. 16 tokens are taken one at a time as
+ *                   generation proceeds) and "Example" (a new token is placed in
+ *                   the sequence's current physical block).
+ *   pa_decode    -- single-query attention for every sequence straight over the
+ *                   paged pool.  Defined by "PagedAttention and KV memory
+ *                   management", section "The kernel side": read the sequence's
+ *                   block table, load each physical block's K and V tiles in
+ *                   turn, and compute scores and weighted values without first
+ *                   gathering the KV into one buffer.
+ *
+ * Layout (all row-major; the same on every entry point):
+ *   k_cache  [num_blocks, num_kv_heads, block_size, head_dim]   kv dtype
+ *   v_cache  [num_blocks, num_kv_heads, head_dim, block_size]   kv dtype
+ *   A slot is physical_block * block_size + offset_in_block.
+ *   Query head h reads KV head h / (num_heads / num_kv_heads).
+ *   out = softmax(scale * q . K^T) . V over positions 0 .. context_len-1.
+ *
+ * Pointers: every array argument is DEVICE memory on the current HIP device,
+ * owned by the caller.  The library allocates nothing, keeps no pointer after
+ * a call returns, and never synchronises.  Each call enqueues its kernels on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns at once;
+ * ordering between calls comes from the stream.
+ *
+ * Errors: argument errors are reported synchronously, before anything is
+ * enqueued, as a nonzero pa_status; pa_last_error() then gives a message
+ * (thread-local, valid until the next call on that thread).  A launch
+ * failure is PA_ERR_LAUNCH.  No C++ exception crosses this interface.
+ *
+ * Device-side data (slots, block ids, context lengths) are not checked on the
+ * host.  The kernels never access memory outside the arrays described by the
+ * size arguments: a slot outside [0, num_blocks*block_size) is not written, a
+ * block id outside [0, num_blocks) is not read (that block then contributes
+ * nothing), and a context length is clamped to [0, max_blocks_per_seq *
+ * block_size].  Such inputs still give an unspecified result for the affected
+ * sequence.  Two tokens with the same slot in one pa_write_kv call race.
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k_cache, v_cache, k_new, v_new.  out is always fp32. */
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,   /* IEEE binary32 */
+  PA_DTYPE_BF16 = 1   /* bfloat16: the top 16 bits of a binary32 */
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, Hq % Hkv != 0, ... */
+  PA_ERR_UNSUPPORTED = 2,   /* (dtype, head_dim, block_size, group size) not compiled */
+  PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = 4         /* the HIP runtime refused a kernel launch */
+} pa_status;
+
+/*
+ * Slot write.  For t in [0, num_tokens): if slot_mapping[t] >= 0, with
+ * b = slot / block_size and o = slot % block_size,
+ *   k_cache[b, h, o, :] = k_new[t, h, :]   and   v_cache[b, h, :, o] = v_new[t, h, :]
+ * for every KV head h.  The copy moves raw element bits (NaN payloads
+ * included).  A negative slot is skipped.  Slots must be distinct.
+ *
+ *   k_new, v_new   [num_tokens, num_kv_heads, head_dim]  kv dtype, device
+ *   slot_mapping   [num_tokens] int32, device
+ *   num_tokens == 0 is a successful no-op (pointers may then be NULL).
+ * Supported: kv_dtype F32 or BF16, any head_dim in [1, 1024], any block_size >= 1.
+ */
+int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these shapes (0 is never
+ * returned for valid shapes; an invalid shape returns 0).  The workspace
+ * holds per-partition softmax states (max, sum, weighted sum) of sequences
+ * whose context is split across workgroups.  Its contents need no
+ * initialisation and are meaningless between calls.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t kv_dtype);
+
+/*
+ * Decode attention.  For every sequence s and query head h, with
+ * L = context_lens[s] (counting the token written by this step's pa_write_kv)
+ * and kv = h / (num_heads / num_kv_heads):
+ *   out[s, h, :] = sum_t softmax_t(scale * q[s,h,:] . K_s[t,kv,:]) * V_s[t,kv,:],  t < L
+ * where position t of sequence s lives in block block_tables[s, t / block_size]
+ * at offset t % block_size.  L == 0 gives out[s, :, :] = 0.
+ *
+ *   out            [num_seqs, num_heads, head_dim] fp32, device (written)
+ *   q              [num_seqs, num_heads, head_dim] kv dtype, device
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32, device; entries past
+ *                  ceil(L / block_size) are never read (padding, e.g. -1)
+ *   context_lens   [num_seqs] int32, device
+ *   workspace      device, at least pa_decode_workspace_bytes(...) bytes
+ *   num_seqs == 0 is a successful no-op.
+ * Compiled: head_dim in {64, 128}, block_size in {16, 32}, group size
+ * num_heads / num_kv_heads in [1, 16], kv_dtype F32 or BF16.
+ * The reduction order depends only on logical positions, so results are
+ * bitwise reproducible and independent of where the blocks sit in the pool.
+ */
+int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode with the context split made explicit, for tests and tuning.
+ * partition_tokens: tokens handled by one workgroup (a multiple of
+ * block_size, or 0 for the library's choice).  flags: PA_FLAG_VECTOR_ALU
+ * selects the plain vector-ALU kernel also for bf16 (by default bf16 uses the
+ * matrix-core kernel).  The workspace must hold
+ * pa_decode_workspace_bytes_ex(..., partition_tokens) bytes.
+ */
+#define PA_FLAG_VECTOR_ALU 1
+int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                 int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks,
+                 int32_t kv_dtype, void* workspace, size_t workspace_bytes,
+                 int32_t partition_tokens, int32_t flags, void* stream);
+
+size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t kv_dtype,
+                                    int32_t partition_tokens);
+
+/* Tokens per partition that pa_decode picks for these shapes (0 if invalid). */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_blocks_per_seq, int32_t block_size);
+
+/* Static description of a status code. */
+const char* pa_status_string(int32_t status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

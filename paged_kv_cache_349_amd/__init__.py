@@ -1,0 +1,187 @@
+"""MI355X (gfx950) paged decode attention: Python binding of libpa.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/paged_attention.h.  PyTorch provides device memory
+and the stream.  There is no fallback: if the library is missing, every call
+raises.
+
+    write_kv(k_cache, v_cache, k_new, v_new, slot_mapping)
+    decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size)
+
+Layouts: k_cache [NB, Hkv, bs, D], v_cache [NB, Hkv, D, bs] (float32 or
+bfloat16); q [S, Hq, D] and k_new/v_new [T, Hkv, D] in the cache dtype;
+out [S, Hq, D] float32; block_tables [S, max_blocks] int32; context_lens [S]
+int32; slot_mapping [T] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "lib", "libpa.so")
+
+PA_DTYPE_F32 = 0
+PA_DTYPE_BF16 = 1
+PA_FLAG_VECTOR_ALU = 1
+
+_STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
+           4: "PA_ERR_LAUNCH"}
+
+_lib = None
+
+_c_int = ctypes.c_int32
+_vp = ctypes.c_void_p
+_SIGNATURES = {
+    "pa_write_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_int, _vp]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 7),
+    "pa_decode_workspace_bytes_ex": (ctypes.c_size_t, [_c_int] * 8),
+    "pa_decode_partition_tokens": (_c_int, [_c_int] * 4),
+    "pa_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float] + [_c_int] * 8 +
+                  [_vp, ctypes.c_size_t, _vp]),
+    "pa_decode_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float] + [_c_int] * 8 +
+                     [_vp, ctypes.c_size_t, _c_int, _c_int, _vp]),
+    "pa_status_string": (ctypes.c_char_p, [_c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpa.so (built by paged_kv_cache_349_amd.build / __graft_entry__.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_349_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().pa_last_error().decode()
+        if status in (1, 2, 3):
+            raise ValueError(f"{_STATUS.get(status)}: {msg}")
+        raise PagedAttentionError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return PA_DTYPE_BF16
+    raise ValueError(f"unsupported KV dtype {t.dtype}")
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        _need(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+    return dev
+
+
+def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
+    """Copy new tokens' K/V into their slots (raw bits; slot < 0 skipped)."""
+    torch = _torch()
+    lib = load_library()
+    dev = _on_gpu(k_cache, v_cache, k_new, v_new, slot_mapping)
+    _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-D")
+    NB, Hkv, bs, D = k_cache.shape
+    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtype mismatch")
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1, "slot_mapping: int32 [T]")
+    T = slot_mapping.shape[0]
+    _need(tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D),
+          "k_new/v_new must be [T, Hkv, D]")
+    _check(lib.pa_write_kv(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                           v_new.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, bs,
+                           _dtype_code(k_cache), _stream_handle(dev, stream)))
+
+
+def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, block_size,
+                    kv_dtype_code, partition_tokens=0) -> int:
+    return int(load_library().pa_decode_workspace_bytes_ex(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, block_size, kv_dtype_code,
+        partition_tokens))
+
+
+_workspaces = {}
+
+
+def _workspace(dev, nbytes):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    key = dev.index
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None,
+           *, workspace=None, partition_tokens=0, vector_alu=False):
+    """Single-query attention per sequence over the paged KV pool; writes `out`."""
+    torch = _torch()
+    lib = load_library()
+    dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, bs, D = k_cache.shape
+    _need(bs == block_size, f"block_size={block_size} but k_cache has {bs}")
+    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
+    S, Hq, _ = q.shape
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, D), "out: float32 [S, Hq, D]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens: int32 [S]")
+    code = _dtype_code(k_cache)
+    max_blocks = block_tables.shape[1]
+    need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code, partition_tokens)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    flags = PA_FLAG_VECTOR_ALU if vector_alu else 0
+    _check(lib.pa_decode_ex(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, S,
+                            Hq, Hkv, D, max_blocks, NB, code, ws_ptr, ws_len, partition_tokens,
+                            flags, _stream_handle(dev, stream)))
+    return out
+
+
+__all__ = ["write_kv", "decode", "workspace_bytes", "load_library", "LIB_PATH",
+           "PagedAttentionError"]

@@ -1,0 +1,214 @@
+// C ABI of libpa.so: argument checks, partition choice, dispatch.
+// The declarations and the contract live in include/paged_attention.h.
+#include "paged_attention.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// Tokens per workgroup partition.  Each (sequence, KV head) pair already
+// gives one workgroup per partition; with few pairs (a small batch or one
+// long context) a shorter partition spreads a sequence over more compute
+// units.  The heuristic sees only host-known shapes.
+int32_t choose_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  int32_t tokens = pairs >= 1024 ? 512 : 256;
+  if (tokens < block_size) tokens = block_size;
+  return tokens - tokens % block_size;
+}
+
+struct Layout {
+  int32_t part_blocks = 0;
+  int32_t num_parts_max = 0;
+  size_t acc_bytes = 0;
+  size_t total = 0;
+};
+
+Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t max_blocks, int32_t block_size, int32_t partition_tokens) {
+  Layout l;
+  l.part_blocks = partition_tokens / block_size;
+  l.num_parts_max = (max_blocks + l.part_blocks - 1) / l.part_blocks;
+  if (l.num_parts_max <= 1) return l;  // one partition: out is written directly
+  const size_t rows = (size_t)num_seqs * num_heads * l.num_parts_max;
+  l.acc_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
+  l.total = l.acc_bytes + rows * 2 * sizeof(float);
+  return l;
+}
+
+bool shapes_valid(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t max_blocks, int32_t block_size) {
+  return num_seqs >= 0 && num_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_blocks > 0 &&
+         block_size > 0 && num_heads % num_kv_heads == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "success";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype/shape combination";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                void* stream) {
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
+  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
+  if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "sizes must be positive (num_blocks=%d num_kv_heads=%d head_dim=%d block_size=%d)",
+                num_blocks, num_kv_heads, head_dim, block_size);
+  if (head_dim > 1024) return fail(PA_ERR_UNSUPPORTED, "head_dim=%d > 1024", head_dim);
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "null device pointer with num_tokens=%d", num_tokens);
+  hipError_t e = pa::launch_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                                     num_blocks, num_kv_heads, head_dim, block_size,
+                                     (pa::KvType)kv_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "write_kv launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_blocks_per_seq, int32_t block_size) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
+  return choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+}
+
+size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t kv_dtype,
+                                    int32_t partition_tokens) {
+  (void)kv_dtype;
+  if (!shapes_valid(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size))
+    return 0;
+  if (partition_tokens == 0)
+    partition_tokens = choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+  if (partition_tokens < block_size || partition_tokens % block_size != 0) return 0;
+  return workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                          partition_tokens)
+      .total;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t kv_dtype) {
+  return pa_decode_workspace_bytes_ex(num_seqs, num_heads, num_kv_heads, head_dim,
+                                      max_blocks_per_seq, block_size, kv_dtype, 0);
+}
+
+int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* context_lens, float scale,
+                 int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks,
+                 int32_t kv_dtype, void* workspace, size_t workspace_bytes,
+                 int32_t partition_tokens, int32_t flags, void* stream) {
+  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
+  if (num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "sizes must be positive (num_heads=%d num_kv_heads=%d head_dim=%d block_size=%d "
+                "max_blocks_per_seq=%d num_blocks=%d)",
+                num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads=%d is not a multiple of num_kv_heads=%d",
+                num_heads, num_kv_heads);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (flags & ~PA_FLAG_VECTOR_ALU) return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const int32_t group = num_heads / num_kv_heads;
+  if (!pa::decode_supported((pa::KvType)kv_dtype, head_dim, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "no kernel for head_dim=%d block_size=%d group=%d (compiled: head_dim 64/128, "
+                "block_size 16/32, group 1..16)",
+                head_dim, block_size, group);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
+      (int64_t)num_seqs * num_heads * head_dim > INT32_MAX * 4LL)
+    return fail(PA_ERR_UNSUPPORTED, "shape too large");
+  if (partition_tokens == 0)
+    partition_tokens = choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+  if (partition_tokens < block_size || partition_tokens % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_tokens=%d is not a positive multiple of %d",
+                partition_tokens, block_size);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null device pointer");
+  const Layout lay = workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                      block_size, partition_tokens);
+  if (lay.total > 0 && (!workspace || workspace_bytes < lay.total))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, lay.total);
+  if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.scale_log2 = (float)((double)scale * kLog2e);
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.part_blocks = lay.part_blocks;
+  p.num_parts_max = lay.num_parts_max;
+  p.ws_acc = lay.total ? (float*)workspace : nullptr;
+  p.ws_ml = lay.total ? (float*)((char*)workspace + lay.acc_bytes) : nullptr;
+  hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
+                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                      num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                      num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, stream);
+}
+
+}  // extern "C"
