@@ -1,0 +1,280 @@
+"""Benchmark of the paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--block-size 16|32]
+
+One step = one pa_write_kv (the new token of every sequence goes into its
+slot) + one pa_decode (single-query attention of every sequence over the
+paged pool), on one HIP stream, over the large-batch GQA workload:
+256 sequences, context lengths lognormal(6.9, 0.6) clipped to [16, 8192],
+64 query heads / 8 KV heads, head_dim 128, block size 16, bf16 K/V/q, fp32
+output, a shuffled pool with 3% free blocks.  Inputs are seeded synthetic
+draws, resident in HBM before the timed region.
+
+Printed: one JSON line on stdout.  Progress goes to stderr.
+
+  value        KV bytes read per step / wall time per step (GB/s): K
+               steps between two device synchronisations.
+  roofline     the decode kernel alone: algorithmic bytes per launch (live
+               K/V tokens + q + out + live block-table entries) / its mean
+               duration from HIP events on the launch stream, against the
+               8 TB/s HBM peak.  `traffic` is the HBM bytes per launch that
+               the FETCH_SIZE / WRITE_SIZE counters measured, scaled by a
+               plain-copy calibration, read from profiles/ and reported only
+               while the kernel source is unchanged since it was measured.
+  cpu_baseline the float64 CPU oracle (one thread) on the whole step.
+
+The contiguous comparison runs the same decode kernel over the same tokens
+packed sequence by sequence in logical order (identity-like tables).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV GB/s (% of HBM peak) and seq-steps/s at 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+DECODE_SOURCES = ["paged_kv_cache_349_amd/csrc/pa_decode.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_large_batch_gqa.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--block-size", type=int, default=16, choices=(16, 32))
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-contig", action="store_true")
+    p.add_argument("--cold-iters", type=int, default=20,
+                   help="decode launches timed after flushing the caches (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the paged decode step runs and is timed on a single MI355X.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd import workloads as wl
+    from paged_kv_cache_349_amd.device_io import upload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t = time.perf_counter()
+    w = wl.make_config(5, block_size=args.block_size, seed=args.seed)
+    log(f"workload {w.name}: S={w.num_seqs} NB={w.num_blocks} max_blocks={w.max_blocks} "
+        f"tokens={int(w.context_lens.sum())} ({time.perf_counter() - t:.1f} s)")
+    d = upload(w, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def write():
+        pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+
+    def decode(dd=d, ww=w):
+        pa.decode(dd.out, dd.q, dd.k_cache, dd.v_cache, dd.block_tables, dd.context_lens,
+                  float(ww.scale), ww.block_size)
+
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        write()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    write_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(K)]
+    decode_us = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(K)]
+    log(f"timed {K} steps: {wall * 1e3 / K:.1f} us/step, decode mean {statistics.mean(decode_us):.1f} us")
+
+    out_gpu = d.out.cpu().numpy().astype(np.float64)
+
+    kv_bytes = w.kv_bytes_logical()
+    alg_bytes = kv_bytes + w.small_bytes()
+    ms_per_step = wall * 1e3 / K
+    dec_mean = statistics.mean(decode_us)
+    dec_med = statistics.median(decode_us)
+    qs = np.percentile(decode_us, [10, 90])
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
+            "context_tokens": int(w.context_lens.sum()), "max_context": int(w.context_lens.max()),
+            "partition_tokens": int(pa.load_library().pa_decode_partition_tokens(
+                w.num_seqs, w.num_kv_heads, w.max_blocks, w.block_size)),
+            "seed": args.seed if args.seed is not None else wl.SEED_BASE + 5,
+        },
+        "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak_step": round(100 * (alg_bytes + w.write_bytes()) / (ms_per_step * 1e-3) /
+                                   (HBM_PEAK_GBPS * 1e9), 2),
+        "decode_us": {"mean": round(dec_mean, 2), "median": round(dec_med, 2),
+                      "p10": round(float(qs[0]), 2), "p90": round(float(qs[1]), 2)},
+        "write_us_mean": round(statistics.mean(write_us), 2),
+        "kv_gbps_decode": round(kv_bytes / (dec_med * 1e-6) / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(alg_bytes / (dec_mean * 1e-6) / 1e9, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(alg_bytes / (dec_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(w.name),
+            "kernel": "pa_decode (decode_mfma_bf16 + merge_partitions)",
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+    }
+
+    # Decode alone with the caches flushed before each launch (1 GiB write
+    # outside the event pair): the 256 MB last-level cache holds a fifth of
+    # this workload's KV, so warm and cold should be close.
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(args.cold_iters):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            decode()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        del flush
+        result["decode_us_cold_median"] = round(statistics.median(cold), 2)
+        log(f"cold decode median {statistics.median(cold):.1f} us")
+
+    if not args.no_contig:
+        wc = wl.to_contiguous(w)
+        dc = upload(wc, dev)
+        pa.write_kv(dc.k_cache, dc.v_cache, dc.k_new, dc.v_new, dc.slot_mapping)
+        for _ in range(args.warmup):
+            decode(dc, wc)
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            evc[i][0].record(stream)
+            decode(dc, wc)
+            evc[i][1].record(stream)
+        torch.cuda.synchronize()
+        contig_us = statistics.mean(evc[i][0].elapsed_time(evc[i][1]) * 1e3 for i in range(K))
+        out_c = dc.out.cpu().numpy()
+        result["contig_decode_us_mean"] = round(contig_us, 2)
+        result["paged_overhead_vs_contig"] = round(dec_mean / contig_us - 1.0, 4)
+        result["contig_output_bitwise_equal"] = bool(
+            np.array_equal(out_c.view(np.uint32), d.out.cpu().numpy().view(np.uint32)))
+        log(f"contiguous decode mean {contig_us:.1f} us, overhead {dec_mean / contig_us - 1:.2%}")
+        del dc
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: one 1 GiB device copy done")
+
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        import oracle
+        reps = []
+        with threadpool_limits(1):
+            for r in range(3):
+                t = time.perf_counter()
+                kr, vr = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping,
+                                         w.block_size)
+                ref = oracle.decode(w.q, kr, vr, w.block_tables, w.context_lens, w.scale,
+                                    w.block_size, w.kv_dtype)
+                reps.append(time.perf_counter() - t)
+                log(f"oracle step {r}: {reps[-1]:.2f} s")
+        tcpu = statistics.median(reps)
+        result["cpu_baseline"] = {
+            "value": round(kv_bytes / tcpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole step (write + decode of all {w.num_seqs} sequences, "
+                      f"{int(w.context_lens.sum())} context tokens), median of 3, NumPy BLAS "
+                      f"limited to 1 thread; host has {len(os.sched_getaffinity(0))} usable cores",
+            "seq_steps_per_s": round(w.num_seqs / tcpu, 2),
+        }
+        err = float(np.abs(out_gpu - ref).max())
+        result["max_abs_err_vs_oracle"] = float(f"{err:.3e}")
+        log(f"max-abs err vs oracle {err:.3e}")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
