@@ -76,7 +76,12 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--block-size", type=int, default=16, choices=(16, 32))
+    p.add_argument("--config", type=int, default=5, choices=(2, 3, 4, 5),
+                   help="workload to time (5, the large-batch GQA decode, is the headline; "
+                        "the others are for diagnosis)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--partition-tokens", type=int, default=0,
+                   help="tokens per decode work item (0 = the library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-contig", action="store_true")
     p.add_argument("--cold-iters", type=int, default=20,
@@ -112,7 +117,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
 
     t = time.perf_counter()
-    w = wl.make_config(5, block_size=args.block_size, seed=args.seed)
+    w = wl.make_config(args.config, block_size=args.block_size, seed=args.seed)
     log(f"workload {w.name}: S={w.num_seqs} NB={w.num_blocks} max_blocks={w.max_blocks} "
         f"tokens={int(w.context_lens.sum())} ({time.perf_counter() - t:.1f} s)")
     d = upload(w, dev)
@@ -123,7 +128,7 @@ def main() -> int:
 
     def decode(dd=d, ww=w):
         pa.decode(dd.out, dd.q, dd.k_cache, dd.v_cache, dd.block_tables, dd.context_lens,
-                  float(ww.scale), ww.block_size)
+                  float(ww.scale), ww.block_size, partition_tokens=args.partition_tokens)
 
     for _ in range(args.warmup):
         write()
@@ -150,7 +155,9 @@ def main() -> int:
     out_gpu = d.out.cpu().numpy().astype(np.float64)
 
     kv_bytes = w.kv_bytes_logical()
-    alg_bytes = kv_bytes + w.small_bytes()
+    # Algorithmic minimum: distinct live K/V positions (blocks shared by
+    # several sequences counted once) + q + out + live table entries.
+    alg_bytes = w.kv_bytes_unique() + w.small_bytes()
     ms_per_step = wall * 1e3 / K
     dec_mean = statistics.mean(decode_us)
     dec_med = statistics.median(decode_us)
@@ -174,9 +181,8 @@ def main() -> int:
             "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "num_blocks": w.num_blocks,
             "context_tokens": int(w.context_lens.sum()), "max_context": int(w.context_lens.max()),
-            "partition_tokens": int(pa.load_library().pa_decode_partition_tokens(
-                w.num_seqs, w.num_kv_heads, w.max_blocks, w.block_size)),
-            "seed": args.seed if args.seed is not None else wl.SEED_BASE + 5,
+            "partition_tokens": args.partition_tokens or "adaptive",
+            "seed": args.seed if args.seed is not None else wl.SEED_BASE + args.config,
         },
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak_step": round(100 * (alg_bytes + w.write_bytes()) / (ms_per_step * 1e-3) /
@@ -192,7 +198,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(alg_bytes / (dec_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(w.name),
-            "kernel": "pa_decode (decode_mfma_bf16 + merge_partitions)",
+            "kernel": "pa_decode (plan_items + decode_mfma_bf16 + merge_splits)",
             "algorithmic_bytes_per_launch": alg_bytes,
         },
     }

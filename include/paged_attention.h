@@ -86,11 +86,13 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
                 void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for these shapes (0 is never
- * returned for valid shapes; an invalid shape returns 0).  The workspace
- * holds per-partition softmax states (max, sum, weighted sum) of sequences
- * whose context is split across workgroups.  Its contents need no
- * initialisation and are meaningless between calls.
+ * Bytes of device workspace pa_decode needs for these shapes (an invalid
+ * shape returns 0).  The workspace holds the call's work list, its counters
+ * and the softmax states (max, sum, weighted sum) of context partitions that
+ * are merged across workgroups.  Every call initialises what it uses: the
+ * contents need no initialisation and are meaningless between calls.  Calls
+ * that may run at the same time (different streams) need separate
+ * workspaces; calls ordered on one stream may share one.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq,

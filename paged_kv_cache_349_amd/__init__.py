@@ -136,14 +136,14 @@ def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, blo
         partition_tokens))
 
 
+# One workspace per (device, stream): calls on one stream run in order, so
+# they may share it; calls on different streams may overlap, so they do not.
 _workspaces = {}
 
 
-def _workspace(dev, nbytes):
+def _workspace(dev, stream_handle, nbytes):
     torch = _torch()
-    if nbytes == 0:
-        return None
-    key = dev.index
+    key = (dev.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -171,15 +171,16 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code, partition_tokens)
+    sh = _stream_handle(dev, stream)
     if workspace is None:
-        workspace = _workspace(dev, need)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        workspace = _workspace(dev, sh, need)
+    ws_ptr = workspace.data_ptr()
+    ws_len = workspace.numel() * workspace.element_size()
     flags = PA_FLAG_VECTOR_ALU if vector_alu else 0
     _check(lib.pa_decode_ex(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, S,
                             Hq, Hkv, D, max_blocks, NB, code, ws_ptr, ws_len, partition_tokens,
-                            flags, _stream_handle(dev, stream)))
+                            flags, sh))
     return out
 
 

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 
 #include "pa_internal.h"
@@ -29,33 +30,52 @@ int ok() {
 
 constexpr double kLog2e = 1.4426950408889634;
 
-// Tokens per workgroup partition.  Each (sequence, KV head) pair already
-// gives one workgroup per partition; with few pairs (a small batch or one
-// long context) a shorter partition spreads a sequence over more compute
-// units.  The heuristic sees only host-known shapes.
-int32_t choose_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size) {
-  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  int32_t tokens = pairs >= 1024 ? 512 : 256;
-  if (tokens < block_size) tokens = block_size;
-  return tokens - tokens % block_size;
+// Partition (work item) size.  With partition_tokens == 0 the decode
+// planner picks, on the device from the actual context lengths, a power-of-two
+// multiple of the smallest size below, up to the largest, such that one
+// partition is at most 1/kBalance of a workgroup's share of the work.  The
+// workspace is sized for the smallest.
+constexpr int32_t kMinPartitionTokens = 256;
+constexpr int32_t kMaxPartitionTokens = 8192;
+constexpr int32_t kBalance = 4;
+
+int32_t min_partition_tokens(int32_t block_size) {
+  const int32_t t = kMinPartitionTokens < block_size ? block_size : kMinPartitionTokens;
+  return t - t % block_size;
 }
 
+// Workspace regions, each 256-byte aligned: planner outputs, work list, list
+// of split sequences, and (when a sequence may span several partitions) the
+// partition states.
 struct Layout {
   int32_t part_blocks = 0;
   int32_t num_parts_max = 0;
-  size_t acc_bytes = 0;
+  size_t ctrl_off = 0, items_off = 0, split_off = 0, acc_off = 0, ml_off = 0;
   size_t total = 0;
 };
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                         int32_t max_blocks, int32_t block_size, int32_t partition_tokens) {
   Layout l;
   l.part_blocks = partition_tokens / block_size;
   l.num_parts_max = (max_blocks + l.part_blocks - 1) / l.part_blocks;
-  if (l.num_parts_max <= 1) return l;  // one partition: out is written directly
-  const size_t rows = (size_t)num_seqs * num_heads * l.num_parts_max;
-  l.acc_bytes = (rows * head_dim * sizeof(float) + 255) / 256 * 256;
-  l.total = l.acc_bytes + rows * 2 * sizeof(float);
+  size_t off = 0;
+  l.ctrl_off = off;
+  off += align256(pa::kCtrlSize * sizeof(int32_t));
+  l.items_off = off;
+  off += align256((size_t)num_seqs * l.num_parts_max * 2 * sizeof(int32_t));
+  l.split_off = off;
+  off += align256((size_t)num_seqs * sizeof(int32_t));
+  if (l.num_parts_max > 1) {
+    const size_t rows = (size_t)num_seqs * num_heads * l.num_parts_max;
+    l.acc_off = off;
+    off += align256(rows * head_dim * sizeof(float));
+    l.ml_off = off;
+    off += align256(rows * 2 * sizeof(float));
+  }
+  l.total = off;
   return l;
 }
 
@@ -107,7 +127,7 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_blocks_per_seq, int32_t block_size) {
   if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;
-  return choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+  return min_partition_tokens(block_size);
 }
 
 size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -117,8 +137,7 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
   (void)kv_dtype;
   if (!shapes_valid(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size))
     return 0;
-  if (partition_tokens == 0)
-    partition_tokens = choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+  if (partition_tokens == 0) partition_tokens = min_partition_tokens(block_size);
   if (partition_tokens < block_size || partition_tokens % block_size != 0) return 0;
   return workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
                           partition_tokens)
@@ -161,21 +180,24 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
       (int64_t)num_seqs * num_heads * head_dim > INT32_MAX * 4LL)
     return fail(PA_ERR_UNSUPPORTED, "shape too large");
-  if (partition_tokens == 0)
-    partition_tokens = choose_partition_tokens(num_seqs, num_kv_heads, block_size);
+  const bool adaptive = partition_tokens == 0;
+  if (adaptive) partition_tokens = min_partition_tokens(block_size);
   if (partition_tokens < block_size || partition_tokens % block_size != 0)
     return fail(PA_ERR_INVALID_ARG, "partition_tokens=%d is not a positive multiple of %d",
                 partition_tokens, block_size);
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "null device pointer");
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
   const Layout lay = workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq,
                                       block_size, partition_tokens);
-  if (lay.total > 0 && (!workspace || workspace_bytes < lay.total))
+  if (!workspace || workspace_bytes < lay.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                 workspace_bytes, workspace, lay.total);
-  if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > INT32_MAX)
-    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > (INT32_MAX >> 1) ||
+      (int64_t)max_blocks_per_seq * num_seqs > (INT32_MAX >> 1))
+    return fail(PA_ERR_UNSUPPORTED, "too many work items");
 
   pa::DecodeParams p;
   p.out = out;
@@ -191,10 +213,18 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
   p.group = group;
   p.max_blocks = max_blocks_per_seq;
   p.num_blocks = num_blocks;
-  p.part_blocks = lay.part_blocks;
+  p.part_blocks_min = lay.part_blocks;
+  const int32_t max_tokens = kMaxPartitionTokens < block_size ? block_size : kMaxPartitionTokens;
+  p.part_blocks_max = adaptive ? max_tokens / block_size : lay.part_blocks;
   p.num_parts_max = lay.num_parts_max;
-  p.ws_acc = lay.total ? (float*)workspace : nullptr;
-  p.ws_ml = lay.total ? (float*)((char*)workspace + lay.acc_bytes) : nullptr;
+  p.balance = adaptive ? kBalance : 0;
+  p.decode_grid = 0;
+  char* ws = (char*)workspace;
+  p.ws_ctrl = (int32_t*)(ws + lay.ctrl_off);
+  p.ws_items = (int2*)(ws + lay.items_off);
+  p.ws_split = (int32_t*)(ws + lay.split_off);
+  p.ws_acc = lay.num_parts_max > 1 ? (float*)(ws + lay.acc_off) : nullptr;
+  p.ws_ml = lay.num_parts_max > 1 ? (float*)(ws + lay.ml_off) : nullptr;
   hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
                                    (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));

@@ -5,15 +5,31 @@
 // K and V tiles in turn, and computes scores and weighted values without
 // first gathering the KV into one buffer.
 //
-// Work split.  One workgroup of W waves owns (sequence s, KV head h,
-// partition p): p covers part_blocks consecutive logical blocks.  Wave w of
-// the workgroup takes blocks p*part_blocks + w, + w + W, ... and keeps a
-// running softmax state (max m, sum l, weighted sum acc) per query head of
-// the group.  At the end the W wave states are merged through LDS in wave
-// order.  A sequence with one partition writes `out` directly; otherwise the
-// partition's state goes to the workspace and merge_partitions() combines the
-// partitions with a log-sum-exp merge, in partition order.  Every reduction
-// order depends on logical positions only.
+// Work items.  A sequence's context is cut into partitions of part_blocks
+// logical blocks; one work item is (sequence s, KV head h, partition p).
+// The cut depends only on the sequence's own length, so every reduction
+// order below depends only on logical positions: results are bitwise
+// reproducible, independent of where blocks sit in the pool and of the
+// other sequences in the batch.
+//
+// Two launches on the caller's stream:
+//   plan_items    one workgroup.  Lists the non-empty (s, p) pairs in the
+//                 workspace -- every full partition first (sequence order),
+//                 then the partial last partitions in decreasing size -- and
+//                 clears the merge counters.
+//   decode_*      persistent: as many workgroups as fit on the chip at once,
+//                 dealt the list round-robin, so no workgroup is launched for
+//                 an empty partition and the work per workgroup stays even
+//                 however ragged the context lengths are.
+//
+// Inside an item, wave w of the W waves takes logical blocks
+// b0 + w, b0 + w + W, ... and keeps a running softmax state (max m, sum l,
+// weighted sum acc) per query head of the group; the W states are merged
+// through LDS in wave order.  A sequence with one partition writes `out`
+// directly.  Otherwise the item stores its partition state in the workspace
+// and bumps the (s, h) arrival counter; the workgroup that brings it to the
+// partition count merges all partitions of (s, h) with a log-sum-exp
+// combination, in partition order, and writes `out`.
 //
 // Matrix-core kernel (bf16).  For each 16-token sub-block:
 //   S^T[16 tokens x 16 heads] = K[16 x D] * Q^T[D x 16]      (v_mfma_f32_16x16x32_bf16)
@@ -28,9 +44,13 @@
 // P is rounded to bf16 for the PV product; the softmax denominator sums those
 // same rounded weights, so the output is an exact convex combination of them.
 //
-// Vector-ALU kernel (fp32, and bf16 on request): the same work split and
-// merge; scores by lanes over tokens, weighted values by lanes over features.
+// Vector-ALU kernel (fp32, and bf16 on request): the same items and merge;
+// scores by lanes over tokens, weighted values by lanes over features.
 #include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "pa_internal.h"
 
@@ -42,6 +62,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kMaxGroup = 16;   // query heads per KV head the kernels handle
+constexpr int kWaves = 4;       // waves per decode workgroup
+constexpr int kTailClasses = 256;
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -63,33 +85,191 @@ __device__ __forceinline__ float widen<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float widen<uint16_t>(uint16_t x) { return bf16_bits_to_f32(x); }
 
-// Shared tail of both kernels: merge the W wave states of this workgroup
-// (wave order), then either finish the sequence (one partition) or store the
-// partition state for merge_partitions().
-//   sm_m, sm_l: [W][kMaxGroup]; sm_acc: [W][group][D + 4]
+__device__ __forceinline__ int clamp_len(const DecodeParams& a, int s, int block_size) {
+  const int L = a.lens[s];
+  const int Lmax = a.max_blocks * block_size;
+  return L < 0 ? 0 : (L > Lmax ? Lmax : L);
+}
+
+// ---------------------------------------------------------------------------
+// Work list.
+// ---------------------------------------------------------------------------
+
+// Block-wide sum over the planner's 1024 threads (16 waves).
+__device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch16[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) t += scratch16[w];
+  return t;
+}
+
+constexpr int kPartChoices = 8;
+
+__global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
+  __shared__ int cls_off[kTailClasses];
+  __shared__ int wave_sum[16];
+  __shared__ int run_base;
+  __shared__ int nsplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.num_seqs;
+
+  for (int i = tid; i < kTailClasses; i += 1024) cls_off[i] = 0;
+  if (tid == 0) {
+    run_base = 0;
+    nsplit = 0;
+  }
+
+  // Partition size: the largest pb = part_blocks_min * 2^k (<= part_blocks_max)
+  // whose partitions are each at most 1/balance of one workgroup's share of
+  // all blocks.  Long partitions mean few partition states to merge; short
+  // ones spread a long context over many workgroups.
+  int pb = a.part_blocks_min;
+  if (a.balance > 0 && a.part_blocks_max > pb) {
+    int mine = 0;     // S * max_blocks fits in int32 (checked on the host)
+    for (int s = tid; s < S; s += 1024)
+      mine += (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+    const int64_t total = block_sum_1024(mine, wave_sum);
+    const int64_t share = total * a.num_kv_heads / ((int64_t)a.decode_grid * a.balance);
+    for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share &&
+                    pb * 2 <= a.part_blocks_max; ++k)
+      pb *= 2;
+  }
+  if (tid == 0) a.ws_ctrl[kCtrlPartBlocks] = pb;
+  __syncthreads();
+
+  // Partial last partition of a sequence: size class, larger partitions in
+  // lower classes.  -1 if the sequence has no partial partition.
+  auto tail_class = [&](int nblk) {
+    const int rem = nblk % pb;
+    if (rem == 0) return -1;
+    return (int)((int64_t)(pb - rem) * (kTailClasses - 1) / pb);
+  };
+
+  // Pass 1: full partitions in sequence order (an empty sequence gets one
+  // item that zeroes its output); count partial partitions per class; list
+  // the sequences that span several partitions.
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int s = c0 + tid;
+    int nfull = 0;
+    if (s < S) {
+      const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+      nfull = nblk == 0 ? 1 : nblk / pb;
+      const int c = tail_class(nblk);
+      if (c >= 0) atomicAdd(&cls_off[c], 1);
+      if (nblk > pb) a.ws_split[atomicAdd(&nsplit, 1)] = s;
+    }
+    int incl = nfull;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int w = 0; w < 16; ++w) {
+      before += w < wave ? wave_sum[w] : 0;
+      chunk += wave_sum[w];
+    }
+    const int base = run_base + before + incl - nfull;
+    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int2(s, p);
+    __syncthreads();
+    if (tid == 0) run_base += chunk;
+    __syncthreads();
+  }
+
+  // Class start offsets after the full partitions.
+  if (tid == 0) {
+    int off = run_base;
+    for (int c = 0; c < kTailClasses; ++c) {
+      const int n = cls_off[c];
+      cls_off[c] = off;
+      off += n;
+    }
+    a.ws_ctrl[kCtrlEntries] = off;
+    a.ws_ctrl[kCtrlSplits] = nsplit;
+  }
+  __syncthreads();
+
+  // Pass 2: partial partitions.  The order inside a class is arbitrary; it
+  // changes which workgroup computes an item, never the result.
+  for (int s = tid; s < S; s += 1024) {
+    const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+    const int c = tail_class(nblk);
+    if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int2(s, nblk / pb);
+  }
+}
+
+struct Item {
+  int s, h, part, L, nblk, b0, b1, nparts;
+};
+
+__device__ __forceinline__ Item make_item(const DecodeParams& a, int2 e, int h, int block_size,
+                                          int pb) {
+  Item it;
+  it.s = e.x;
+  it.part = e.y;
+  it.h = h;
+  it.L = clamp_len(a, it.s, block_size);
+  it.nblk = (it.L + block_size - 1) / block_size;
+  it.b0 = it.part * pb;
+  it.b1 = min(it.b0 + pb, it.nblk);
+  it.nparts = (it.nblk + pb - 1) / pb;
+  return it;
+}
+
+// LDS areas shared by both kernels (floats): sm_m, sm_l [W][kMaxGroup],
+// sm_acc [W][group][D + 4].
 template <int D, int W>
-__device__ __forceinline__ void finish_partition(const DecodeParams& a, const float* sm_m,
-                                                 const float* sm_l, const float* sm_acc, int s,
-                                                 int h, int part, int nparts) {
+struct Lds {
+  float* m;
+  float* l;
+  float* acc;
+  __device__ Lds(float* smem, int group) : m(smem), l(smem + W * kMaxGroup),
+                                           acc(smem + 2 * W * kMaxGroup) {
+    (void)group;
+  }
+};
+
+// Zero output of a sequence with no tokens.
+template <int D, int W>
+__device__ __forceinline__ void zero_item(const DecodeParams& a, const Item& it) {
   const int G = a.group;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * W)
+    a.out[((int64_t)it.s * a.num_heads + it.h * G) * D + idx] = 0.f;
+}
+
+// Merge the W wave states of this item (wave order), then either finish the
+// sequence (one partition) or store the partition state for merge_splits().
+template <int D, int W>
+__device__ void finish_item(const DecodeParams& a, const Lds<D, W>& sm, const Item& it) {
+  const int G = a.group;
+  const bool split = it.nparts > 1;
+  const int64_t prow = ((int64_t)it.s * a.num_kv_heads + it.h) * a.num_parts_max;
+#pragma unroll 1
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
     const int g = idx / D;
     const int d = idx - g * D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w * kMaxGroup + g]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.m[w * kMaxGroup + g]);
     float lam = 0.f, val = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float mw = sm_m[w * kMaxGroup + g];
+      const float mw = sm.m[w * kMaxGroup + g];
       const float c = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-      lam += sm_l[w * kMaxGroup + g] * c;
-      val += sm_acc[(w * G + g) * (D + 4) + d] * c;
+      lam += sm.l[w * kMaxGroup + g] * c;
+      val += sm.acc[(w * G + g) * (D + 4) + d] * c;
     }
-    if (nparts == 1) {
-      a.out[((int64_t)s * a.num_heads + h * G + g) * D + d] = lam > 0.f ? val / lam : 0.f;
+    if (!split) {
+      a.out[((int64_t)it.s * a.num_heads + it.h * G + g) * D + d] = lam > 0.f ? val / lam : 0.f;
     } else {
-      const int64_t row = (((int64_t)s * a.num_kv_heads + h) * a.num_parts_max + part) * G + g;
+      const int64_t row = (prow + it.part) * G + g;
       a.ws_acc[row * D + d] = val;
       if (d == 0) {
         a.ws_ml[row * 2 + 0] = M;
@@ -99,36 +279,30 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& a, const fl
   }
 }
 
-// Zero output of a sequence with no tokens (written by partition 0).
-template <int D, int W>
-__device__ __forceinline__ void zero_sequence(const DecodeParams& a, int s, int h) {
-  const int G = a.group;
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * W)
-    a.out[((int64_t)s * a.num_heads + h * G) * D + idx] = 0.f;
-}
-
-// Decode the flat workgroup index into (partition, sequence, KV head) and the
-// partition's block range.  Returns false if the workgroup has nothing to do.
-struct WorkItem {
-  int s, h, part, L, nblk, b0, b1, nparts;
-};
-
-__device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& a, int block_size) {
-  WorkItem it;
-  const int idx = blockIdx.x;
-  it.part = idx % a.num_parts_max;
-  const int rest = idx / a.num_parts_max;
-  it.s = rest % a.num_seqs;
-  it.h = rest / a.num_seqs;
-  int L = a.lens[it.s];
-  const int Lmax = a.max_blocks * block_size;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  it.L = L;
-  it.nblk = (L + block_size - 1) / block_size;
-  it.b0 = it.part * a.part_blocks;
-  it.b1 = min(it.b0 + a.part_blocks, it.nblk);
-  it.nparts = (it.nblk + a.part_blocks - 1) / a.part_blocks;
-  return it;
+// Persistent item loop shared by both kernels: workgroup b takes list items
+// b, b + G, b + 2G, ... (G = grid size, all resident at once).  The list
+// holds full partitions first and partial ones in decreasing size, so the
+// round-robin deal evens out the work per workgroup without any shared
+// counter: the workgroups left one full partition short are the first to
+// receive the largest partial ones.
+template <int D, int W, typename Body>
+__device__ __forceinline__ void run_items(const DecodeParams& a, int block_size, float* smem,
+                                          Body body) {
+  const int Hkv = a.num_kv_heads;
+  const int total = a.ws_ctrl[kCtrlEntries] * Hkv;
+  const int pb = a.ws_ctrl[kCtrlPartBlocks];
+  const Lds<D, W> sm(smem, a.group);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int e_idx = item / Hkv;
+    const Item it = make_item(a, a.ws_items[e_idx], item - e_idx * Hkv, block_size, pb);
+    if (it.nblk == 0) {
+      zero_item<D, W>(a, it);
+    } else {
+      body(it, sm);              // leaves the wave states in LDS, then syncs
+      finish_item<D, W>(a, sm, it);
+    }
+    __syncthreads();             // LDS is reused by the next item
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -161,15 +335,8 @@ __device__ __forceinline__ void load_tile(Tile<D, BS>& t, const uint16_t* __rest
 }
 
 template <int D, int BS, int W>
-__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
-  extern __shared__ float smem[];
-  const WorkItem it = decode_work_item(a, BS);
-  if (it.nblk == 0) {
-    if (it.part == 0) zero_sequence<D, W>(a, it.s, it.h);
-    return;
-  }
-  if (it.b0 >= it.nblk) return;
-
+__device__ __forceinline__ void mfma_item(const DecodeParams& a, const Item& it,
+                                          const Lds<D, W>& sm) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, quad = lane >> 4;
@@ -297,20 +464,24 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
 
-  float* sm_m = smem;
-  float* sm_l = smem + W * kMaxGroup;
-  float* sm_acc = smem + 2 * W * kMaxGroup;
   if (quad == 0) {
-    sm_m[w * kMaxGroup + g] = m;
-    sm_l[w * kMaxGroup + g] = lsum;
+    sm.m[w * kMaxGroup + g] = m;
+    sm.l[w * kMaxGroup + g] = lsum;
   }
   if (g < G) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
-      *reinterpret_cast<f32x4*>(&sm_acc[(w * G + g) * (D + 4) + i * 16 + quad * 4]) = acc[i];
+      *reinterpret_cast<f32x4*>(&sm.acc[(w * G + g) * (D + 4) + i * 16 + quad * 4]) = acc[i];
   }
   __syncthreads();
-  finish_partition<D, W>(a, sm_m, sm_l, sm_acc, it.s, it.h, it.part, it.nparts);
+}
+
+template <int D, int BS, int W>
+__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
+  extern __shared__ float smem[];
+  run_items<D, W>(a, BS, smem, [&](const Item& it, const Lds<D, W>& sm) {
+    mfma_item<D, BS, W>(a, it, sm);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -318,15 +489,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 // ---------------------------------------------------------------------------
 
 template <typename T, int D, int BS, int W>
-__global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
-  extern __shared__ float smem[];
-  const WorkItem it = decode_work_item(a, BS);
-  if (it.nblk == 0) {
-    if (it.part == 0) zero_sequence<D, W>(a, it.s, it.h);
-    return;
-  }
-  if (it.b0 >= it.nblk) return;
-
+__device__ __forceinline__ void valu_item(const DecodeParams& a, const Item& it,
+                                          const Lds<D, W>& sm, float* smem) {
   constexpr int NC = 64 / BS;          // lanes per token in the score step
   constexpr int DC = D / NC;           // features per lane in the score step
   constexpr int DL = D / 64;           // features per lane in the weighted sum
@@ -336,11 +500,8 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
   const int Hkv = a.num_kv_heads;
   const int tt = lane % BS, ch = lane / BS;
 
-  float* sm_m = smem;
-  float* sm_l = smem + W * kMaxGroup;
-  float* sm_acc = smem + 2 * W * kMaxGroup;            // [W][G][D+4]
-  float* sm_q = sm_acc + W * G * (D + 4);              // [G][D]
-  float* sm_p = sm_q + G * D;                          // [W][kMaxGroup][BS]
+  float* sm_q = smem + 2 * W * kMaxGroup + W * G * (D + 4);   // [G][D]
+  float* sm_p = sm_q + G * D;                                 // [W][kMaxGroup][BS]
 
   const T* qrow = (const T*)a.q + ((int64_t)it.s * a.num_heads + it.h * G) * D;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) sm_q[idx] = widen<T>(qrow[idx]);
@@ -418,50 +579,65 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) l += shfl_xor_f(l, off);
     if (lane == 0) {
-      sm_m[w * kMaxGroup + g] = m[g];
-      sm_l[w * kMaxGroup + g] = l;
+      sm.m[w * kMaxGroup + g] = m[g];
+      sm.l[w * kMaxGroup + g] = l;
     }
 #pragma unroll
-    for (int k = 0; k < DL; ++k) sm_acc[(w * G + g) * (D + 4) + lane + 64 * k] = acc[g][k];
+    for (int k = 0; k < DL; ++k) sm.acc[(w * G + g) * (D + 4) + lane + 64 * k] = acc[g][k];
   }
   __syncthreads();
-  finish_partition<D, W>(a, sm_m, sm_l, sm_acc, it.s, it.h, it.part, it.nparts);
+}
+
+template <typename T, int D, int BS, int W>
+__global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
+  extern __shared__ float smem[];
+  run_items<D, W>(a, BS, smem, [&](const Item& it, const Lds<D, W>& sm) {
+    valu_item<T, D, BS, W>(a, it, sm, smem);
+  });
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of a sequence's partitions, in partition order.
+// Log-sum-exp merge of the partition states of split sequences, in
+// partition order: with M = max_p m_p, out = sum_p 2^(m_p - M) acc_p /
+// sum_p 2^(m_p - M) l_p.  One workgroup per (split sequence, KV head), four
+// features per thread.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void merge_partitions(DecodeParams a, int head_dim,
-                                                        int block_size) {
-  const int s = blockIdx.x % a.num_seqs;
-  const int h = blockIdx.x / a.num_seqs;
-  int L = a.lens[s];
-  const int Lmax = a.max_blocks * block_size;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int nblk = (L + block_size - 1) / block_size;
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-  if (nparts <= 1) return;
-  const int G = a.group, D = head_dim;
-  const int64_t row0 = ((int64_t)s * a.num_kv_heads + h) * a.num_parts_max;
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = kNegInf;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_ml[((row0 + p) * G + g) * 2]);
-    float lam = 0.f, val = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const int64_t row = (row0 + p) * G + g;
-      const float mp = a.ws_ml[row * 2];
-      const float c = (mp == kNegInf) ? 0.f : exp2_fast(mp - M);
-      lam += a.ws_ml[row * 2 + 1] * c;
-      val += a.ws_acc[row * D + d] * c;
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits(DecodeParams a, int block_size) {
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+  const int Hkv = a.num_kv_heads, G = a.group;
+  const int total = a.ws_ctrl[kCtrlSplits] * Hkv;
+  const int pb = a.ws_ctrl[kCtrlPartBlocks];
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int s = a.ws_split[item / Hkv];
+    const int h = item % Hkv;
+    const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+    const int nparts = (nblk + pb - 1) / pb;
+    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
+    for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
+      const int g = idx / (D / 4);
+      const int d4 = idx - g * (D / 4);
+      float M = kNegInf;
+      for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_ml[((prow + p) * G + g) * 2]);
+      float lam = 0.f;
+      f4 val = {0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < nparts; ++p) {
+        const int64_t row = (prow + p) * G + g;
+        const float mp = a.ws_ml[row * 2];
+        const float c = (mp == kNegInf) ? 0.f : exp2_fast(mp - M);
+        lam += a.ws_ml[row * 2 + 1] * c;
+        val += *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4) * c;
+      }
+      const f4 o = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) = o;
     }
-    a.out[((int64_t)s * a.num_heads + h * G + g) * D + d] = lam > 0.f ? val / lam : 0.f;
   }
 }
 
-constexpr int kWaves = 4;
+// ---------------------------------------------------------------------------
+// Launch.
+// ---------------------------------------------------------------------------
 
 template <int D>
 size_t smem_bytes(int group, bool valu, int block_size) {
@@ -470,24 +646,64 @@ size_t smem_bytes(int group, bool valu, int block_size) {
   return f * sizeof(float);
 }
 
+// Workgroups of `kernel` that fit on the current device at once.
+int resident_workgroups(const void* kernel, int threads, size_t smem) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(dev, kernel, smem);
+  std::lock_guard<std::mutex> lock(mu);
+  auto found = cache.find(key);
+  if (found != cache.end()) return found->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, smem) != hipSuccess)
+    return 0;
+  const int n = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+  cache.emplace(key, n);
+  return n;
+}
+
 template <int D, int BS>
-hipError_t launch_decode_shape(const DecodeParams& p, KvType type, bool vector_alu,
+hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_alu,
                                hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)p.num_parts_max * p.num_seqs * p.num_kv_heads);
+  const int threads = 64 * kWaves;
+  const void* kernel;
+  size_t smem;
   if (type == KvType::BF16 && !vector_alu) {
-    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves>), dim3(grid), dim3(64 * kWaves),
-                       smem_bytes<D>(p.group, false, BS), stream, p);
+    kernel = (const void*)decode_mfma_bf16<D, BS, kWaves>;
+    smem = smem_bytes<D>(p0.group, false, BS);
   } else if (type == KvType::BF16) {
-    hipLaunchKernelGGL((decode_valu<uint16_t, D, BS, kWaves>), dim3(grid), dim3(64 * kWaves),
-                       smem_bytes<D>(p.group, true, BS), stream, p);
+    kernel = (const void*)decode_valu<uint16_t, D, BS, kWaves>;
+    smem = smem_bytes<D>(p0.group, true, BS);
   } else {
-    hipLaunchKernelGGL((decode_valu<float, D, BS, kWaves>), dim3(grid), dim3(64 * kWaves),
-                       smem_bytes<D>(p.group, true, BS), stream, p);
+    kernel = (const void*)decode_valu<float, D, BS, kWaves>;
+    smem = smem_bytes<D>(p0.group, true, BS);
   }
+  const int resident = resident_workgroups(kernel, threads, smem);
+  if (resident <= 0) return hipErrorInvalidDeviceFunction;
+  DecodeParams p = p0;
+  const int64_t max_items = (int64_t)p.num_seqs * p.num_parts_max * p.num_kv_heads;
+  p.decode_grid = (int)(max_items < resident ? max_items : resident);
+
+  hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (type == KvType::BF16 && !vector_alu)
+    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),
+                       smem, stream, p);
+  else if (type == KvType::BF16)
+    hipLaunchKernelGGL((decode_valu<uint16_t, D, BS, kWaves>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else
+    hipLaunchKernelGGL((decode_valu<float, D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),
+                       smem, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
-  hipLaunchKernelGGL(merge_partitions, dim3((unsigned)(p.num_seqs * p.num_kv_heads)), dim3(256),
-                     0, stream, p, D, BS);
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  const unsigned mgrid = (unsigned)(pairs < 2048 ? pairs : 2048);
+  hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p, BS);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -23,11 +24,25 @@ struct DecodeParams {
   int32_t group;              // num_heads / num_kv_heads, 1..16
   int32_t max_blocks;         // table row length
   int32_t num_blocks;         // pool size, for the block-id range check
-  int32_t part_blocks;        // blocks per partition (one workgroup each)
-  int32_t num_parts_max;      // ceil(max_blocks / part_blocks)
+  int32_t part_blocks_min;    // smallest partition the planner may pick (sizes the workspace)
+  int32_t part_blocks_max;    // largest partition the planner may pick
+  int32_t num_parts_max;      // ceil(max_blocks / part_blocks_min): partition-state row stride
+  int32_t balance;            // planner: the largest item is at most 1/balance of a
+                              // workgroup's share of the work (0: always part_blocks_min)
+  int32_t decode_grid;        // workgroups of the decode launch (set by the launcher)
   float* ws_acc;              // [S, Hkv, num_parts_max, group, D] partition sums
   float* ws_ml;               // [S, Hkv, num_parts_max, group, 2] partition (max, sum)
+  int2* ws_items;             // [S * num_parts_max] work list of (sequence, partition)
+  int32_t* ws_split;          // [S] sequences spanning more than one partition
+  int32_t* ws_ctrl;           // [kCtrlSize] written by the planner
 };
+
+// ws_ctrl slots written by the planner: work-list entries, chosen partition
+// size in blocks, number of split sequences.
+constexpr int kCtrlEntries = 0;
+constexpr int kCtrlPartBlocks = 1;
+constexpr int kCtrlSplits = 2;
+constexpr int kCtrlSize = 4;
 
 enum class KvType { F32 = 0, BF16 = 1 };
 

@@ -52,17 +52,26 @@ def test_status_strings(lib):
     assert lib.pa_status_string(99) == b"unknown status"
 
 
+def _align(n):
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_sizes(lib):
-    # one partition per sequence -> no workspace at all
-    assert lib.pa_decode_workspace_bytes_ex(4, 8, 8, 64, 4, 16, 0, 64) == 0
-    # 256 seqs, 64 heads, D=128, 285 blocks of 16, 512-token partitions -> 9 partitions
+    # one partition per sequence: planner outputs + work list + split list only
+    assert lib.pa_decode_workspace_bytes_ex(4, 8, 8, 64, 4, 16, 0, 64) == \
+        256 + _align(4 * 1 * 8) + _align(4 * 4)
+    # 256 seqs, 64 heads / 8 KV heads, D=128, 285 blocks of 16, 512-token partitions -> 9
     n = lib.pa_decode_workspace_bytes_ex(256, 64, 8, 128, 285, 16, 1, 512)
     rows = 256 * 64 * 9
-    assert n == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    assert n == (256 + _align(256 * 9 * 8) + _align(256 * 4) + _align(rows * 128 * 4) +
+                 _align(rows * 8))
+    # the library's choice is sized for its smallest partition (256 tokens)
+    assert lib.pa_decode_workspace_bytes(256, 64, 8, 128, 285, 16, 1) == \
+        lib.pa_decode_workspace_bytes_ex(256, 64, 8, 128, 285, 16, 1, 256)
     assert lib.pa_decode_workspace_bytes_ex(256, 64, 8, 128, 285, 16, 1, 24) == 0   # not a multiple
     assert lib.pa_decode_workspace_bytes(4, 6, 4, 64, 4, 16, 0) == 0                 # Hq % Hkv
-    assert lib.pa_decode_partition_tokens(256, 8, 285, 16) in (256, 512)
-    assert lib.pa_decode_partition_tokens(256, 8, 285, 32) % 32 == 0
+    assert lib.pa_decode_partition_tokens(256, 8, 285, 16) == 256
+    assert lib.pa_decode_partition_tokens(256, 8, 285, 32) == 256
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
@@ -89,6 +98,8 @@ def _decode(lib, **kw):
     (dict(pt=24), 1),
     (dict(out=None), 1),
     (dict(t=None), 1),
+    (dict(q=FAKE + 4), 1),
+    (dict(out=FAKE + 8), 1),
     (dict(D=96), 2),
     (dict(bs=8), 2),
     (dict(Hq=34, Hkv=2), 2),
