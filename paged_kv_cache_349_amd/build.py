@@ -24,8 +24,11 @@ LIB = os.path.join(LIBDIR, "libpa.so")
 ARCH = "gfx950"
 SOURCES = ["pa_api.cpp", "pa_write_kv.hip", "pa_decode.hip"]
 # Packed fp32 instructions are kept out of the device code.
+# MFMA accumulators are kept in ordinary VGPRs, where the softmax rescale can
+# reach them without copies to and from the accumulation registers.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -37,7 +37,7 @@ constexpr double kLog2e = 1.4426950408889634;
 // workspace is sized for the smallest.
 constexpr int32_t kMinPartitionTokens = 256;
 constexpr int32_t kMaxPartitionTokens = 8192;
-constexpr int32_t kBalance = 4;
+constexpr int32_t kBalance = 2;
 
 int32_t min_partition_tokens(int32_t block_size) {
   const int32_t t = kMinPartitionTokens < block_size ? block_size : kMinPartitionTokens;
@@ -65,9 +65,9 @@ Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
   l.ctrl_off = off;
   off += align256(pa::kCtrlSize * sizeof(int32_t));
   l.items_off = off;
-  off += align256((size_t)num_seqs * l.num_parts_max * 2 * sizeof(int32_t));
+  off += align256((size_t)num_seqs * l.num_parts_max * 4 * sizeof(int32_t));
   l.split_off = off;
-  off += align256((size_t)num_seqs * sizeof(int32_t));
+  off += align256((size_t)num_seqs * 2 * sizeof(int32_t));
   if (l.num_parts_max > 1) {
     const size_t rows = (size_t)num_seqs * num_heads * l.num_parts_max;
     l.acc_off = off;
@@ -221,8 +221,8 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
   p.decode_grid = 0;
   char* ws = (char*)workspace;
   p.ws_ctrl = (int32_t*)(ws + lay.ctrl_off);
-  p.ws_items = (int2*)(ws + lay.items_off);
-  p.ws_split = (int32_t*)(ws + lay.split_off);
+  p.ws_items = (int4*)(ws + lay.items_off);
+  p.ws_split = (int2*)(ws + lay.split_off);
   p.ws_acc = lay.num_parts_max > 1 ? (float*)(ws + lay.acc_off) : nullptr;
   p.ws_ml = lay.num_parts_max > 1 ? (float*)(ws + lay.ml_off) : nullptr;
   hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,

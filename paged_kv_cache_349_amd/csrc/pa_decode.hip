@@ -18,9 +18,9 @@
 //                 then the partial last partitions in decreasing size -- and
 //                 clears the merge counters.
 //   decode_*      persistent: as many workgroups as fit on the chip at once,
-//                 dealt the list round-robin, so no workgroup is launched for
-//                 an empty partition and the work per workgroup stays even
-//                 however ragged the context lengths are.
+//                 dealt the list in snake order, so no workgroup is launched
+//                 for an empty partition and the work per workgroup stays
+//                 even however ragged the context lengths are.
 //
 // Inside an item, wave w of the W waves takes logical blocks
 // b0 + w, b0 + w + W, ... and keeps a running softmax state (max m, sum l,
@@ -64,6 +64,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kMaxGroup = 16;   // query heads per KV head the kernels handle
 constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kTailClasses = 256;
+constexpr int kMaxLdsSlots = 2;    // LDS state slots of the matrix-core kernel (power of 2)
+constexpr int kMaxLdsRecords = 16; // LDS output records of the matrix-core kernel
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
       nfull = nblk == 0 ? 1 : nblk / pb;
       const int c = tail_class(nblk);
       if (c >= 0) atomicAdd(&cls_off[c], 1);
-      if (nblk > pb) a.ws_split[atomicAdd(&nsplit, 1)] = s;
+      if (nblk > pb) a.ws_split[atomicAdd(&nsplit, 1)] = make_int2(s, (nblk + pb - 1) / pb);
     }
     int incl = nfull;
 #pragma unroll
@@ -177,31 +179,46 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
       chunk += wave_sum[w];
     }
     const int base = run_base + before + incl - nfull;
-    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int2(s, p);
+    if (nfull > 0) {
+      const int L = clamp_len(a, s, block_size);
+      for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, 0);
+    }
     __syncthreads();
     if (tid == 0) run_base += chunk;
     __syncthreads();
   }
 
-  // Class start offsets after the full partitions.
-  if (tid == 0) {
-    int off = run_base;
-    for (int c = 0; c < kTailClasses; ++c) {
-      const int n = cls_off[c];
-      cls_off[c] = off;
-      off += n;
+  // Class start offsets after the full partitions: exclusive scan of the
+  // class counts by the first kTailClasses threads (4 waves).
+  {
+    const int n = tid < kTailClasses ? cls_off[tid] : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-    a.ws_ctrl[kCtrlEntries] = off;
-    a.ws_ctrl[kCtrlSplits] = nsplit;
+    if (lane == 63 && wave < kTailClasses / 64) wave_sum[wave] = incl;
+    __syncthreads();
+    if (tid < kTailClasses) {
+      int before = run_base;
+      for (int w = 0; w < wave; ++w) before += wave_sum[w];
+      cls_off[tid] = before + incl - n;
+      if (tid == kTailClasses - 1) {
+        a.ws_ctrl[kCtrlEntries] = before + incl;
+        a.ws_ctrl[kCtrlSplits] = nsplit;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // Pass 2: partial partitions.  The order inside a class is arbitrary; it
   // changes which workgroup computes an item, never the result.
   for (int s = tid; s < S; s += 1024) {
-    const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+    const int L = clamp_len(a, s, block_size);
+    const int nblk = (L + block_size - 1) / block_size;
     const int c = tail_class(nblk);
-    if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int2(s, nblk / pb);
+    if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int4(s, nblk / pb, L, 0);
   }
 }
 
@@ -209,13 +226,12 @@ struct Item {
   int s, h, part, L, nblk, b0, b1, nparts;
 };
 
-__device__ __forceinline__ Item make_item(const DecodeParams& a, int2 e, int h, int block_size,
-                                          int pb) {
+__device__ __forceinline__ Item make_item(int4 e, int h, int block_size, int pb) {
   Item it;
   it.s = e.x;
   it.part = e.y;
   it.h = h;
-  it.L = clamp_len(a, it.s, block_size);
+  it.L = e.z;
   it.nblk = (it.L + block_size - 1) / block_size;
   it.b0 = it.part * pb;
   it.b1 = min(it.b0 + pb, it.nblk);
@@ -223,15 +239,28 @@ __device__ __forceinline__ Item make_item(const DecodeParams& a, int2 e, int h, 
   return it;
 }
 
-// LDS areas shared by both kernels (floats): sm_m, sm_l [W][kMaxGroup],
-// sm_acc [W][group][D + 4].
+// LDS area of the wave states of one item: m, l [W][kMaxGroup] and acc
+// [W][group][D + 4] floats.  The vector-ALU kernel adds its own scratch
+// after one such area; the matrix-core kernel keeps two (item parity).
+template <int D, int W>
+__host__ __device__ constexpr int lds_state_floats(int group) {
+  return 2 * W * kMaxGroup + W * group * (D + 4);
+}
+
+// LDS output record of one merged item (floats): G*D values, (max, sum)
+// per head, and a 4-int header (sequence, KV head, partition, split flag).
+template <int D>
+__host__ __device__ constexpr int lds_record_floats(int group) {
+  return group * D + 2 * kMaxGroup + 4;
+}
+
 template <int D, int W>
 struct Lds {
   float* m;
   float* l;
   float* acc;
-  __device__ Lds(float* smem, int group) : m(smem), l(smem + W * kMaxGroup),
-                                           acc(smem + 2 * W * kMaxGroup) {
+  __device__ Lds(float* smem, int group)
+      : m(smem), l(smem + W * kMaxGroup), acc(smem + 2 * W * kMaxGroup) {
     (void)group;
   }
 };
@@ -279,12 +308,12 @@ __device__ void finish_item(const DecodeParams& a, const Lds<D, W>& sm, const It
   }
 }
 
-// Persistent item loop shared by both kernels: workgroup b takes list items
-// b, b + G, b + 2G, ... (G = grid size, all resident at once).  The list
-// holds full partitions first and partial ones in decreasing size, so the
-// round-robin deal evens out the work per workgroup without any shared
-// counter: the workgroups left one full partition short are the first to
-// receive the largest partial ones.
+// Persistent item loop shared by both kernels.  The list (full partitions
+// first, then partial ones in decreasing size) is dealt to the G resident
+// workgroups in snake order -- round r gives item r*G + b to workgroup b
+// when r is even and to workgroup G-1-b when r is odd -- which evens out the
+// work per workgroup without any shared counter.  Once a workgroup's item
+// is past the end, so are all its later ones.
 template <int D, int W, typename Body>
 __device__ __forceinline__ void run_items(const DecodeParams& a, int block_size, float* smem,
                                           Body body) {
@@ -292,9 +321,12 @@ __device__ __forceinline__ void run_items(const DecodeParams& a, int block_size,
   const int total = a.ws_ctrl[kCtrlEntries] * Hkv;
   const int pb = a.ws_ctrl[kCtrlPartBlocks];
   const Lds<D, W> sm(smem, a.group);
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  const int G = gridDim.x, b = blockIdx.x;
+  for (int r = 0;; ++r) {
+    const int item = r * G + ((r & 1) ? G - 1 - b : b);
+    if (item >= total) break;
     const int e_idx = item / Hkv;
-    const Item it = make_item(a, a.ws_items[e_idx], item - e_idx * Hkv, block_size, pb);
+    const Item it = make_item(a.ws_items[e_idx], item - e_idx * Hkv, block_size, pb);
     if (it.nblk == 0) {
       zero_item<D, W>(a, it);
     } else {
@@ -316,80 +348,161 @@ struct Tile {
   i16x4 v[SB][D / 16];                    // PV A operand: feature (l%16), 4 tokens
 };
 
+// Buffer resource (gfx9 raw buffer: byte-addressed, stride 0) over `bytes`
+// bytes at `base`.  Loads at an offset >= bytes return zero without touching
+// memory, so a resource of 0 bytes reads as all zeros.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+constexpr int kBufferFormatWord = 0x00020000;   // 32-bit data format, no swizzle
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferFormatWord);
+}
+
+// Byte offsets of this lane inside a K tile, a V tile and a query group.
+// Each load is a buffer load: scalar resource + this fixed vector offset +
+// an immediate, so the stream needs no per-load vector address arithmetic.
+struct LaneOff {
+  uint32_t k, v, q;
+};
+
 template <int D, int BS>
-__device__ __forceinline__ void load_tile(Tile<D, BS>& t, const uint16_t* __restrict__ kt,
-                                          const uint16_t* __restrict__ vt, int lane) {
-  const int row = lane & 15, quad = lane >> 4;
+__device__ __forceinline__ LaneOff lane_offsets(int lane, int group) {
+  const uint32_t row = lane & 15, quad = lane >> 4;
+  LaneOff o;
+  o.k = (row * D + quad * 8) * 2;      // K row `row`, features 8*quad ..
+  o.v = (row * BS + quad * 4) * 2;     // V feature `row`, tokens 4*quad ..
+  // Query head `row` of the group; padding heads point past the group so
+  // their loads return zeros.
+  o.q = (int)row < group ? (row * D + quad * 8) * 2 : (uint32_t)group * D * 2;
+  return o;
+}
+
+template <int D, int BS>
+__device__ __forceinline__ void load_tile(Tile<D, BS>& t, __amdgpu_buffer_rsrc_t kr,
+                                          __amdgpu_buffer_rsrc_t vr, const LaneOff& o) {
 #pragma unroll
   for (int sb = 0; sb < Tile<D, BS>::SB; ++sb) {
-    const uint16_t* kr = kt + (sb * 16 + row) * D + quad * 8;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      t.k[sb][c] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + c * 32));
+      t.k[sb][c] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + (sb * 16 * D + c * 32) * 2, 0, 0));
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const uint16_t* vr = vt + (i * 16 + row) * BS + sb * 16 + quad * 4;
-      t.v[sb][i] = __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2*>(vr));
-    }
+    for (int i = 0; i < D / 16; ++i)
+      t.v[sb][i] = __builtin_bit_cast(
+          i16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, o.v + (i * 16 * BS + sb * 16) * 2, 0, 0));
   }
 }
 
+// Read-only views through the constant address space: uniform reads of
+// them become scalar loads, which are counted apart from the vector loads
+// that stream the K/V tiles, so waiting for a block id never drains the tile
+// pipeline.
+#define PA_CONST __attribute__((address_space(4)))
+
+template <typename T>
+__device__ __forceinline__ const PA_CONST T* as_const(const T* p) {
+  return (const PA_CONST T*)(const void PA_CONST*)(uintptr_t)p;
+}
+
+// One work item as a wave sees it (every field is uniform across the wave).
+struct Desc {
+  int s, h, L, b0, nparts, part;
+  int nmine;        // this wave's blocks in the item: b0 + w, b0 + w + W, ...
+  int npos;         // positions the wave spends on the item: max(nmine, 1)
+  bool valid;
+};
+
+// Persistent matrix-core kernel.  Each wave walks one stream of positions:
+// item after item (snake order, as for run_items), one position per block it
+// owns in the item, and one empty position in an item where it owns none.
+// Every step issues the loads of the next position -- which may belong to
+// the next item -- into one register buffer and computes the current
+// position from the other, so the K/V stream keeps flowing across item
+// boundaries.  Each step issues exactly the same loads (a position without a
+// block reads block 0, computed fully masked), so the compiler can count
+// them and wait only for the buffer it uses.  After the last position of an
+// item each wave hands its state to the item's LDS slot; the last wave of
+// the workgroup to do so merges them and writes the result (see finish).
 template <int D, int BS, int W>
-__device__ __forceinline__ void mfma_item(const DecodeParams& a, const Item& it,
-                                          const Lds<D, W>& sm) {
+__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
+  extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, quad = lane >> 4;
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
+  const int NG = gridDim.x, bid = blockIdx.x;
 
-  // Query operand: lane holds q[head g][32c + 8*quad .. +7] (zero for padding heads).
-  bf16x8 qop[D / 32];
-  {
-    const uint16_t* qg =
-        (const uint16_t*)a.q + ((int64_t)it.s * a.num_heads + it.h * G + g) * D + quad * 8;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (g < G) raw = *reinterpret_cast<const uint4*>(qg + c * 32);
-      qop[c] = __builtin_bit_cast(bf16x8, raw);
-    }
+  const PA_CONST int32_t* ctrl = as_const(a.ws_ctrl);
+  const PA_CONST int32_t* items = as_const((const int32_t*)a.ws_items);   // int4 entries
+  const PA_CONST int32_t* tables = as_const(a.tables);
+  const int total = ctrl[kCtrlEntries] * Hkv;
+  const int pb = ctrl[kCtrlPartBlocks];
+
+  auto desc = [&](int r) -> Desc {
+    Desc d;
+    const int item = r * NG + ((r & 1) ? NG - 1 - bid : bid);
+    d.valid = item < total;
+    const int e_idx = d.valid ? item / Hkv : 0;
+    d.s = items[4 * e_idx + 0];
+    d.part = items[4 * e_idx + 1];
+    d.L = d.valid ? items[4 * e_idx + 2] : 0;
+    d.h = d.valid ? item - e_idx * Hkv : 0;
+    const int nblk = (d.L + BS - 1) / BS;
+    d.b0 = d.part * pb;
+    const int nb = min(d.b0 + pb, nblk) - d.b0;
+    d.nparts = (nblk + pb - 1) / pb;
+    d.nmine = nb > w ? (nb - w + W - 1) / W : 0;
+    d.npos = d.nmine > 0 ? d.nmine : 1;
+    return d;
+  };
+
+  Desc cur = desc(0);
+  if (!cur.valid) return;            // no work for this workgroup at all
+  __shared__ int s_count[kMaxLdsSlots];   // waves that finished the slot's item
+  __shared__ int s_epoch[kMaxLdsSlots];   // item the slot is free for
+  if (threadIdx.x < kMaxLdsSlots) {
+    s_count[threadIdx.x] = 0;
+    s_epoch[threadIdx.x] = threadIdx.x;
   }
+  __syncthreads();
+  Desc nxt = desc(1);
+  int r = 0;
 
-  // Block ids of this wave's blocks, 64 at a time, one per lane: lane k of
-  // the current chunk holds the id of the wave's (id_base + k)-th block.
-  const int nmine = (it.b1 - (it.b0 + w) + W - 1) / W;   // may be <= 0
-  const int32_t* trow = a.tables + (int64_t)it.s * a.max_blocks;
-  int id_base = 0;
-  int my_id = -1;
-  if (lane < nmine) my_id = trow[it.b0 + w + lane * W];
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+  const char* qbase = (const char*)a.q;
+  const uint32_t tile_bytes = (uint32_t)BS * D * 2;
+  const LaneOff lo = lane_offsets<D, BS>(lane, G);
 
-  const uint16_t* kbase = (const uint16_t*)a.k_cache;
-  const uint16_t* vbase = (const uint16_t*)a.v_cache;
-  const int64_t tile_elems = (int64_t)BS * D;
+  // Loads of one position into a buffer.  `has` says whether the position
+  // holds a block of the wave; a block id outside the pool counts as none,
+  // and a position without a block reads zeros (a 0-byte resource).
+  auto load_pos = [&](Tile<D, BS>& t, bf16x8* q, const Desc& d, int k, bool& has) {
+    int id = 0;
+    if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + w + k * W];
+    has = d.valid && k < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
+    const int64_t off = has ? ((int64_t)id * Hkv + d.h) * tile_bytes : 0;
+    const uint32_t nb = has ? tile_bytes : 0;
+    load_tile<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo);
+    const __amdgpu_buffer_rsrc_t qr = buffer_of(
+        qbase + ((int64_t)(d.valid ? d.s : 0) * a.num_heads + d.h * G) * D * 2,
+        d.valid ? (uint32_t)G * D * 2 : 0);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      q[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, lo.q + c * 64, 0, 0));
+  };
 
   float m = kNegInf, lsum = 0.f;
   f32x4 acc[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // k increases by one per call, so the next chunk is fetched when k leaves this one.
-  auto tile_ptrs = [&](int k, const uint16_t*& kt, const uint16_t*& vt) -> bool {
-    if (k - id_base >= 64) {
-      id_base += 64;
-      my_id = (id_base + lane < nmine) ? trow[it.b0 + w + (id_base + lane) * W] : -1;
-    }
-    const int id = __builtin_amdgcn_readlane(my_id, k - id_base);
-    if ((unsigned)id >= (unsigned)a.num_blocks) return false;
-    const int64_t tile = (int64_t)id * Hkv + it.h;
-    kt = kbase + tile * tile_elems;
-    vt = vbase + tile * tile_elems;
-    return true;
-  };
-
-  auto compute = [&](Tile<D, BS>& t, int k) {
-    const int j = it.b0 + w + k * W;               // logical block number
-    const int tok0 = j * BS;
+  // One position: scores, online-softmax update, weighted values.  Positions
+  // >= live are masked; live <= 0 masks the whole block.
+  auto compute = [&](Tile<D, BS>& t, const bf16x8* qop, int live) {
     f32x4 sc[Tile<D, BS>::SB];
 #pragma unroll
     for (int sb = 0; sb < Tile<D, BS>::SB; ++sb) {
@@ -398,90 +511,191 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& a, const Item& it,
       for (int c = 0; c < D / 32; ++c)
         sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sb][c], qop[c], sc[sb], 0, 0, 0);
     }
-    // Scale into base-2 units, mask positions >= L (select, never multiply:
+    // Scale into base-2 units, mask dead positions (select, never multiply:
     // the tail of the last block may hold anything), block max per head.
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = tok0 + sb * 16 + quad * 4 + r;
-        const float x = pos < it.L ? sc[sb][r] * a.scale_log2 : kNegInf;
-        sc[sb][r] = x;
+      for (int rr = 0; rr < 4; ++rr) {
+        const float x = sb * 16 + quad * 4 + rr < live ? sc[sb][rr] * a.scale_log2 : kNegInf;
+        sc[sb][rr] = x;
         mx = fmaxf(mx, x);
       }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float mnew = fmaxf(m, mx);
-    const float alpha = exp2_fast(m - mnew);        // 0 on the first block (m = -inf)
+    // Exponent reference: the running max, or 0 while every position seen so
+    // far is masked (then all weights, the rescale factor included, are 0).
+    const float mref = mnew == kNegInf ? 0.f : mnew;
+    const float alpha = exp2_fast(m - mref);       // 0 on the first live block
     m = mnew;
-    i16x4 pb[Tile<D, BS>::SB];
+    i16x4 pw[Tile<D, BS>::SB];
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t b = f32_to_bf16_bits(exp2_fast(sc[sb][r] - mnew));
-        pb[sb][r] = (short)b;
-        psum += bf16_bits_to_f32(b);
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
+        pw[sb][rr] = (short)bits;
+        psum += bf16_bits_to_f32(bits);
       }
     lsum = lsum * alpha + psum;
+    // alpha is exactly 1 for every head whose running max did not move, which
+    // after the first blocks is nearly always: skip the rescale then.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
-    // Last block: zero V of masked positions (their weight is 0, but 0 * NaN is NaN).
-    if (tok0 + BS > it.L) {
+      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+    }
+    // Partly dead block: zero V of dead positions (their weight is 0, but
+    // 0 * NaN is NaN).
+    if (live < BS) {
 #pragma unroll
       for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool dead = tok0 + sb * 16 + quad * 4 + r >= it.L;
+        for (int rr = 0; rr < 4; ++rr) {
+          const bool dead = sb * 16 + quad * 4 + rr >= live;
 #pragma unroll
-          for (int i = 0; i < D / 16; ++i) t.v[sb][i][r] = dead ? (short)0 : t.v[sb][i][r];
+          for (int i = 0; i < D / 16; ++i) t.v[sb][i][rr] = dead ? (short)0 : t.v[sb][i][rr];
         }
     }
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
 #pragma unroll
       for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pb[sb], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[i], 0, 0, 0);
   };
 
-  // Two register tiles: the next block's loads are in flight while the
-  // current one is computed.
-  Tile<D, BS> t0, t1;
-  const uint16_t *kt, *vt;
-  bool ok0 = false, ok1 = false;
-  if (nmine > 0 && (ok0 = tile_ptrs(0, kt, vt))) load_tile<D, BS>(t0, kt, vt, lane);
-  for (int k = 0; k < nmine; k += 2) {
-    if (k + 1 < nmine && (ok1 = tile_ptrs(k + 1, kt, vt))) load_tile<D, BS>(t1, kt, vt, lane);
-    if (ok0) compute(t0, k);
-    if (k + 1 >= nmine) break;
-    if (k + 2 < nmine && (ok0 = tile_ptrs(k + 2, kt, vt))) load_tile<D, BS>(t0, kt, vt, lane);
-    if (ok1) compute(t1, k + 1);
-  }
-
-  // Sum l over the four lane quads that hold the same head.
-  lsum += shfl_xor_f(lsum, 16);
-  lsum += shfl_xor_f(lsum, 32);
-
-  if (quad == 0) {
-    sm.m[w * kMaxGroup + g] = m;
-    sm.l[w * kMaxGroup + g] = lsum;
-  }
-  if (g < G) {
+  // End of an item, without a barrier: the wave stores its state in the
+  // item's LDS state slot and counts itself in; the last of the W waves to
+  // arrive merges the W states (in wave order) into the item's LDS output
+  // record, while the others go straight on with their next item.  Output
+  // records reach global memory only when the record ring is full or the
+  // workgroup's last item is merged: a global store makes the wave's next
+  // wait for a K/V tile also wait for the store (the vector-memory counter
+  // is in order), so stores are kept out of the stream.  Before reusing a
+  // state slot a wave waits until the merge of the slot's previous item is
+  // done; the slowest wave never waits (every slot it needs was freed by
+  // merges of items all waves have passed), so the waits always end.
+  const int state_floats = lds_state_floats<D, W>(G);
+  const int rec_floats = lds_record_floats<D>(G);
+  float* recs = smem + a.lds_slots * state_floats;
+  auto finish = [&](const Desc& d, int r_item, bool wg_last) {
+    const int slot = r_item & (a.lds_slots - 1);
+    const Lds<D, W> sm(smem + slot * state_floats, G);
+    while (__hip_atomic_load(&s_epoch[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+           r_item)
+      __builtin_amdgcn_s_sleep(1);
+    float ls = lsum;
+    ls += shfl_xor_f(ls, 16);
+    ls += shfl_xor_f(ls, 32);
+    if (quad == 0) {
+      sm.m[w * kMaxGroup + g] = m;
+      sm.l[w * kMaxGroup + g] = ls;
+    }
+    if (g < G) {
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      *reinterpret_cast<f32x4*>(&sm.acc[(w * G + g) * (D + 4) + i * 16 + quad * 4]) = acc[i];
-  }
-  __syncthreads();
-}
+      for (int i = 0; i < D / 16; ++i)
+        *reinterpret_cast<f32x4*>(&sm.acc[(w * G + g) * (D + 4) + i * 16 + quad * 4]) = acc[i];
+    }
+    int before = 0;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(&s_count[slot], 1, __ATOMIC_ACQ_REL,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before != W - 1) return;
+    // Last wave: merge into the output record.  Lane (g, quad) handles
+    // features i*16 + 4*quad .. +3 of head g.
+    const int ri = r_item % a.lds_records;
+    float* rec = recs + ri * rec_floats;
+    const bool split = d.nparts > 1;
+    if (g < G) {
+      float M = kNegInf;
+#pragma unroll
+      for (int v = 0; v < W; ++v) M = fmaxf(M, sm.m[v * kMaxGroup + g]);
+      float c[W];
+      float lam = 0.f;
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float mv = sm.m[v * kMaxGroup + g];
+        c[v] = (mv == kNegInf) ? 0.f : exp2_fast(mv - M);
+        lam += sm.l[v * kMaxGroup + g] * c[v];
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < W; ++v)
+          val += *reinterpret_cast<const f32x4*>(&sm.acc[(v * G + g) * (D + 4) + i * 16 +
+                                                         quad * 4]) * c[v];
+        if (!split) val = lam > 0.f ? val / lam : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(&rec[g * D + i * 16 + quad * 4]) = val;
+      }
+      if (quad == 0) {
+        rec[G * D + 2 * g] = M;
+        rec[G * D + 2 * g + 1] = lam;
+      }
+    }
+    if (lane == 0) {
+      int* hdr = reinterpret_cast<int*>(rec + G * D + 2 * kMaxGroup);
+      hdr[0] = d.s;
+      hdr[1] = d.h;
+      hdr[2] = d.part;
+      hdr[3] = split;
+      __hip_atomic_store(&s_count[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(&s_epoch[slot], r_item + a.lds_slots, __ATOMIC_RELEASE,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    // Flush the records of items r_item - ri .. r_item when the ring is full
+    // or this is the workgroup's last item.  Every earlier merge is complete:
+    // its wave merged before it finished this item.
+    if (ri != a.lds_records - 1 && !wg_last) return;
+    for (int j = 0; j <= ri; ++j) {
+      const float* rj = recs + j * rec_floats;
+      const int* hdr = reinterpret_cast<const int*>(rj + G * D + 2 * kMaxGroup);
+      const int s = hdr[0], h = hdr[1], part = hdr[2];
+      const bool sp = hdr[3] != 0;
+      const int64_t row0 = (((int64_t)s * Hkv + h) * a.num_parts_max + part) * G;
+      float* dst = sp ? a.ws_acc + row0 * D : a.out + ((int64_t)s * a.num_heads + h * G) * D;
+      for (int e = lane; e < G * D / 4; e += 64)
+        *reinterpret_cast<f32x4*>(dst + e * 4) = *reinterpret_cast<const f32x4*>(rj + e * 4);
+      if (sp && lane < 2 * G) a.ws_ml[row0 * 2 + lane] = rj[G * D + lane];
+    }
+  };
 
-template <int D, int BS, int W>
-__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
-  extern __shared__ float smem[];
-  run_items<D, W>(a, BS, smem, [&](const Item& it, const Lds<D, W>& sm) {
-    mfma_item<D, BS, W>(a, it, sm);
-  });
+  // The stream.  Position (cur, k); its buffer was loaded one step earlier.
+  Tile<D, BS> t0, t1;
+  bf16x8 q0[D / 32], q1[D / 32];
+  bool has0 = false, has1 = false;
+  int k = 0;
+  load_pos(t0, q0, cur, 0, has0);
+
+  // One step: load the next position into (tn, qn), compute (tc, qc).
+  // Returns false when the stream has ended.
+  auto step = [&](Tile<D, BS>& tc, bf16x8* qc, bool hc, Tile<D, BS>& tn, bf16x8* qn,
+                  bool& hn) -> bool {
+    const bool last = k + 1 >= cur.npos;
+    load_pos(tn, qn, last ? nxt : cur, last ? 0 : k + 1, hn);
+    compute(tc, qc, hc ? cur.L - (cur.b0 + w + k * W) * BS : 0);
+    if (!last) {
+      ++k;
+      return true;
+    }
+    finish(cur, r, !nxt.valid);
+    m = kNegInf;
+    lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!nxt.valid) return false;
+    ++r;
+    cur = nxt;
+    nxt = desc(r + 1);
+    k = 0;
+    return true;
+  };
+
+  while (step(t0, q0, has0, t1, q1, has1) && step(t1, q1, has1, t0, q0, has0)) {
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -604,16 +818,14 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 // ---------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits(DecodeParams a, int block_size) {
+__global__ __launch_bounds__(256) void merge_splits(DecodeParams a) {
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
   const int Hkv = a.num_kv_heads, G = a.group;
   const int total = a.ws_ctrl[kCtrlSplits] * Hkv;
-  const int pb = a.ws_ctrl[kCtrlPartBlocks];
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int s = a.ws_split[item / Hkv];
+    const int2 e = a.ws_split[item / Hkv];
+    const int s = e.x, nparts = e.y;
     const int h = item % Hkv;
-    const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
-    const int nparts = (nblk + pb - 1) / pb;
     const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
     for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
       const int g = idx / (D / 4);
@@ -640,10 +852,26 @@ __global__ __launch_bounds__(256) void merge_splits(DecodeParams a, int block_si
 // ---------------------------------------------------------------------------
 
 template <int D>
-size_t smem_bytes(int group, bool valu, int block_size) {
-  size_t f = 2 * kWaves * kMaxGroup + (size_t)kWaves * group * (D + 4);
-  if (valu) f += (size_t)group * D + (size_t)kWaves * kMaxGroup * block_size;
-  return f * sizeof(float);
+size_t smem_bytes(int group, bool valu, int block_size, int lds_slots, int lds_records) {
+  const size_t state = lds_state_floats<D, kWaves>(group);
+  if (valu) return (state + (size_t)group * D + (size_t)kWaves * kMaxGroup * block_size) * 4;
+  return ((size_t)lds_slots * state + (size_t)lds_records * lds_record_floats<D>(group)) * 4;
+}
+
+// LDS of the matrix-core kernel: two state slots and as many output records
+// (up to kMaxLdsRecords) as keep it within 74 KB, so that two workgroups fit
+// in one CU's 160 KB; a single slot when two slots and one record do not fit.
+template <int D>
+void lds_layout_for(int group, int* slots, int* records) {
+  const int budget = 74 * 1024 / 4;
+  const int state = lds_state_floats<D, kWaves>(group);
+  const int rec = lds_record_floats<D>(group);
+  int ns = 2;
+  if (ns * state + rec > budget) ns = 1;
+  int nr = (budget - ns * state) / rec;
+  nr = nr < 1 ? 1 : (nr > kMaxLdsRecords ? kMaxLdsRecords : nr);
+  *slots = ns;
+  *records = nr;
 }
 
 // Workgroups of `kernel` that fit on the current device at once.
@@ -671,19 +899,20 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   const int threads = 64 * kWaves;
   const void* kernel;
   size_t smem;
+  DecodeParams p = p0;
+  lds_layout_for<D>(p0.group, &p.lds_slots, &p.lds_records);
   if (type == KvType::BF16 && !vector_alu) {
     kernel = (const void*)decode_mfma_bf16<D, BS, kWaves>;
-    smem = smem_bytes<D>(p0.group, false, BS);
+    smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
   } else if (type == KvType::BF16) {
     kernel = (const void*)decode_valu<uint16_t, D, BS, kWaves>;
-    smem = smem_bytes<D>(p0.group, true, BS);
+    smem = smem_bytes<D>(p0.group, true, BS, 0, 0);
   } else {
     kernel = (const void*)decode_valu<float, D, BS, kWaves>;
-    smem = smem_bytes<D>(p0.group, true, BS);
+    smem = smem_bytes<D>(p0.group, true, BS, 0, 0);
   }
   const int resident = resident_workgroups(kernel, threads, smem);
   if (resident <= 0) return hipErrorInvalidDeviceFunction;
-  DecodeParams p = p0;
   const int64_t max_items = (int64_t)p.num_seqs * p.num_parts_max * p.num_kv_heads;
   p.decode_grid = (int)(max_items < resident ? max_items : resident);
 
@@ -703,7 +932,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
   const unsigned mgrid = (unsigned)(pairs < 2048 ? pairs : 2048);
-  hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p, BS);
+  hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -30,10 +30,12 @@ struct DecodeParams {
   int32_t balance;            // planner: the largest item is at most 1/balance of a
                               // workgroup's share of the work (0: always part_blocks_min)
   int32_t decode_grid;        // workgroups of the decode launch (set by the launcher)
+  int32_t lds_slots;          // LDS state slots of the matrix-core kernel (set by the launcher)
+  int32_t lds_records;        // LDS output records of the matrix-core kernel (set by the launcher)
   float* ws_acc;              // [S, Hkv, num_parts_max, group, D] partition sums
   float* ws_ml;               // [S, Hkv, num_parts_max, group, 2] partition (max, sum)
-  int2* ws_items;             // [S * num_parts_max] work list of (sequence, partition)
-  int32_t* ws_split;          // [S] sequences spanning more than one partition
+  int4* ws_items;             // [S * num_parts_max] work list: (sequence, partition, length, 0)
+  int2* ws_split;             // [S] (sequence, partitions) of sequences spanning several
   int32_t* ws_ctrl;           // [kCtrlSize] written by the planner
 };
 

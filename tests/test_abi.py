@@ -59,11 +59,11 @@ def _align(n):
 def test_workspace_sizes(lib):
     # one partition per sequence: planner outputs + work list + split list only
     assert lib.pa_decode_workspace_bytes_ex(4, 8, 8, 64, 4, 16, 0, 64) == \
-        256 + _align(4 * 1 * 8) + _align(4 * 4)
+        256 + _align(4 * 1 * 16) + _align(4 * 8)
     # 256 seqs, 64 heads / 8 KV heads, D=128, 285 blocks of 16, 512-token partitions -> 9
     n = lib.pa_decode_workspace_bytes_ex(256, 64, 8, 128, 285, 16, 1, 512)
     rows = 256 * 64 * 9
-    assert n == (256 + _align(256 * 9 * 8) + _align(256 * 4) + _align(rows * 128 * 4) +
+    assert n == (256 + _align(256 * 9 * 16) + _align(256 * 8) + _align(rows * 128 * 4) +
                  _align(rows * 8))
     # the library's choice is sized for its smallest partition (256 tokens)
     assert lib.pa_decode_workspace_bytes(256, 64, 8, 128, 285, 16, 1) == \
