@@ -203,14 +203,15 @@ def main() -> int:
         },
     }
 
-    # Decode alone with the caches flushed before each launch (1 GiB write
-    # outside the event pair): the 256 MB last-level cache holds a fifth of
-    # this workload's KV, so warm and cold should be close.
+    # Decode alone with the caches flushed before each launch by reading
+    # 1 GiB outside the event pair (a read leaves no dirty lines behind for the
+    # decode to write back): the 256 MB last-level cache holds a fifth of this
+    # workload's KV, so warm and cold should be close.
     if args.cold_iters > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         cold = []
         for _ in range(args.cold_iters):
-            flush.fill_(1)
+            flush.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             decode()
