@@ -32,12 +32,11 @@ constexpr double kLog2e = 1.4426950408889634;
 
 // Partition (work item) size.  With partition_tokens == 0 the decode
 // planner picks, on the device from the actual context lengths, a power-of-two
-// multiple of the smallest size below, up to the largest, such that one
-// partition is at most 1/kBalance of a workgroup's share of the work.  The
-// workspace is sized for the smallest.
+// multiple of the smallest size below, up to the largest, small enough for
+// the work to spread evenly over the resident workgroups (the launcher sets
+// the ratio).  The workspace is sized for the smallest.
 constexpr int32_t kMinPartitionTokens = 256;
 constexpr int32_t kMaxPartitionTokens = 8192;
-constexpr int32_t kBalance = 2;
 
 int32_t min_partition_tokens(int32_t block_size) {
   const int32_t t = kMinPartitionTokens < block_size ? block_size : kMinPartitionTokens;
@@ -217,7 +216,7 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
   const int32_t max_tokens = kMaxPartitionTokens < block_size ? block_size : kMaxPartitionTokens;
   p.part_blocks_max = adaptive ? max_tokens / block_size : lay.part_blocks;
   p.num_parts_max = lay.num_parts_max;
-  p.balance = adaptive ? kBalance : 0;
+  p.balance = adaptive ? 1 : 0;   // the launcher sets the ratio
   p.decode_grid = 0;
   char* ws = (char*)workspace;
   p.ws_ctrl = (int32_t*)(ws + lay.ctrl_off);

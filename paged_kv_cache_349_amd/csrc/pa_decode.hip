@@ -22,10 +22,10 @@
 //                 for an empty partition and the work per workgroup stays
 //                 even however ragged the context lengths are.
 //
-// Inside an item, wave w of the W waves takes logical blocks
-// b0 + w, b0 + w + W, ... and keeps a running softmax state (max m, sum l,
+// Inside an item, the wave in lane j of the W lanes takes logical blocks
+// b0 + j, b0 + j + W, ... and keeps a running softmax state (max m, sum l,
 // weighted sum acc) per query head of the group; the W states are merged
-// through LDS in wave order.  A sequence with one partition writes `out`
+// through LDS in lane order.  A sequence with one partition writes `out`
 // directly.  Otherwise the item stores its partition state in the workspace
 // and bumps the (s, h) arrival counter; the workgroup that brings it to the
 // partition count merges all partitions of (s, h) with a log-sum-exp
@@ -66,6 +66,7 @@ constexpr int kWaves = 4;       // waves per decode workgroup
 constexpr int kTailClasses = 256;
 constexpr int kMaxLdsSlots = 2;    // LDS state slots of the matrix-core kernel (power of 2)
 constexpr int kMaxLdsRecords = 16; // LDS output records of the matrix-core kernel
+constexpr int kSpinLimit = 1 << 22; // polls (~0.1 s) before an LDS wait is declared broken
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -112,7 +113,10 @@ __device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
 
 constexpr int kPartChoices = 8;
 
+constexpr int kLensCached = 8192;   // context lengths the planner keeps in LDS
+
 __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
+  __shared__ int lens_c[kLensCached];
   __shared__ int cls_off[kTailClasses];
   __shared__ int wave_sum[16];
   __shared__ int run_base;
@@ -125,24 +129,33 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
     run_base = 0;
     nsplit = 0;
   }
+  // One pass over the context lengths (clamped), kept in LDS for the passes
+  // below, and the total block count.  S * max_blocks fits in int32 (checked
+  // on the host).
+  int mine = 0;
+  for (int s = tid; s < S; s += 1024) {
+    const int L = clamp_len(a, s, block_size);
+    if (s < kLensCached) lens_c[s] = L;
+    mine += (L + block_size - 1) / block_size;
+  }
+  const int64_t total = block_sum_1024(mine, wave_sum);   // also publishes lens_c
+  auto len_of = [&](int s) { return s < kLensCached ? lens_c[s] : clamp_len(a, s, block_size); };
 
   // Partition size: the largest pb = part_blocks_min * 2^k (<= part_blocks_max)
   // whose partitions are each at most 1/balance of one workgroup's share of
   // all blocks.  Long partitions mean few partition states to merge; short
   // ones spread a long context over many workgroups.
   int pb = a.part_blocks_min;
-  if (a.balance > 0 && a.part_blocks_max > pb) {
-    int mine = 0;     // S * max_blocks fits in int32 (checked on the host)
-    for (int s = tid; s < S; s += 1024)
-      mine += (clamp_len(a, s, block_size) + block_size - 1) / block_size;
-    const int64_t total = block_sum_1024(mine, wave_sum);
+  if (a.balance > 0) {
     const int64_t share = total * a.num_kv_heads / ((int64_t)a.decode_grid * a.balance);
     for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share &&
                     pb * 2 <= a.part_blocks_max; ++k)
       pb *= 2;
   }
-  if (tid == 0) a.ws_ctrl[kCtrlPartBlocks] = pb;
-  __syncthreads();
+  if (tid == 0) {
+    a.ws_ctrl[kCtrlPartBlocks] = pb;
+    a.ws_ctrl[kCtrlAbort] = 0;
+  }
 
   // Partial last partition of a sequence: size class, larger partitions in
   // lower classes.  -1 if the sequence has no partial partition.
@@ -157,9 +170,10 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
   // the sequences that span several partitions.
   for (int c0 = 0; c0 < S; c0 += 1024) {
     const int s = c0 + tid;
-    int nfull = 0;
+    int nfull = 0, L = 0;
     if (s < S) {
-      const int nblk = (clamp_len(a, s, block_size) + block_size - 1) / block_size;
+      L = len_of(s);
+      const int nblk = (L + block_size - 1) / block_size;
       nfull = nblk == 0 ? 1 : nblk / pb;
       const int c = tail_class(nblk);
       if (c >= 0) atomicAdd(&cls_off[c], 1);
@@ -179,10 +193,7 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
       chunk += wave_sum[w];
     }
     const int base = run_base + before + incl - nfull;
-    if (nfull > 0) {
-      const int L = clamp_len(a, s, block_size);
-      for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, 0);
-    }
+    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, 0);
     __syncthreads();
     if (tid == 0) run_base += chunk;
     __syncthreads();
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
   // Pass 2: partial partitions.  The order inside a class is arbitrary; it
   // changes which workgroup computes an item, never the result.
   for (int s = tid; s < S; s += 1024) {
-    const int L = clamp_len(a, s, block_size);
+    const int L = len_of(s);
     const int nblk = (L + block_size - 1) / block_size;
     const int c = tail_class(nblk);
     if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int4(s, nblk / pb, L, 0);
@@ -409,7 +420,8 @@ __device__ __forceinline__ const PA_CONST T* as_const(const T* p) {
 // One work item as a wave sees it (every field is uniform across the wave).
 struct Desc {
   int s, h, L, b0, nparts, part;
-  int nmine;        // this wave's blocks in the item: b0 + w, b0 + w + W, ...
+  int wr;           // the wave's lane in the item: (w + round) mod W
+  int nmine;        // the wave's blocks in the item: b0 + wr, b0 + wr + W, ...
   int npos;         // positions the wave spends on the item: max(nmine, 1)
   bool valid;
 };
@@ -440,10 +452,29 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   const PA_CONST int32_t* tables = as_const(a.tables);
   const int total = ctrl[kCtrlEntries] * Hkv;
   const int pb = ctrl[kCtrlPartBlocks];
+  __shared__ int s_count[kMaxLdsSlots];   // waves that finished the slot's item
+  __shared__ int s_epoch[kMaxLdsSlots];   // item the slot is free for
+
+  // A wait that has not ended after kSpinLimit polls (tens of milliseconds;
+  // a legitimate one lasts microseconds) means a broken invariant: record it
+  // in the workspace and give up, so the kernel still ends.
+  auto abort_wait = [&]() {
+    if (lane == 0) __hip_atomic_store(&a.ws_ctrl[kCtrlAbort], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // The workgroup's item for round r: the list (longest items first) is
+  // dealt to the NG resident workgroups in snake order -- round r gives item
+  // r*NG + b to workgroup b when r is even and to workgroup NG-1-b when r is
+  // odd -- which evens out the work per workgroup without a shared counter.
+  // (A shared counter handing out items on demand was measured slower: the
+  // two workgroups sharing a CU stream at different speeds, and the slower
+  // one then holds long items to the end.)
+  auto item_of = [&](int r) -> int { return r * NG + ((r & 1) ? NG - 1 - bid : bid); };
 
   auto desc = [&](int r) -> Desc {
     Desc d;
-    const int item = r * NG + ((r & 1) ? NG - 1 - bid : bid);
+    const int item = item_of(r);
     d.valid = item < total;
     const int e_idx = d.valid ? item / Hkv : 0;
     d.s = items[4 * e_idx + 0];
@@ -454,21 +485,23 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     d.b0 = d.part * pb;
     const int nb = min(d.b0 + pb, nblk) - d.b0;
     d.nparts = (nblk + pb - 1) / pb;
-    d.nmine = nb > w ? (nb - w + W - 1) / W : 0;
+    // Rotating the waves' lanes from item to item spreads the extra blocks of
+    // items whose size is not a multiple of W evenly over the waves.
+    d.wr = (w + r) & (W - 1);
+    d.nmine = nb > d.wr ? (nb - d.wr + W - 1) / W : 0;
     d.npos = d.nmine > 0 ? d.nmine : 1;
     return d;
   };
 
-  Desc cur = desc(0);
-  if (!cur.valid) return;            // no work for this workgroup at all
-  __shared__ int s_count[kMaxLdsSlots];   // waves that finished the slot's item
-  __shared__ int s_epoch[kMaxLdsSlots];   // item the slot is free for
+  if (bid >= total) return;          // no work for this workgroup at all
   if (threadIdx.x < kMaxLdsSlots) {
     s_count[threadIdx.x] = 0;
     s_epoch[threadIdx.x] = threadIdx.x;
   }
   __syncthreads();
-  Desc nxt = desc(1);
+  Desc cur = desc(0);
+  Desc nxt;               // the next round's item, read when first needed
+  bool have_nxt = false;
   int r = 0;
 
   const char* kbase = (const char*)a.k_cache;
@@ -482,7 +515,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // and a position without a block reads zeros (a 0-byte resource).
   auto load_pos = [&](Tile<D, BS>& t, bf16x8* q, const Desc& d, int k, bool& has) {
     int id = 0;
-    if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + w + k * W];
+    if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + d.wr + k * W];
     has = d.valid && k < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
     const int64_t off = has ? ((int64_t)id * Hkv + d.h) * tile_bytes : 0;
     const uint32_t nb = has ? tile_bytes : 0;
@@ -583,20 +616,28 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   auto finish = [&](const Desc& d, int r_item, bool wg_last) {
     const int slot = r_item & (a.lds_slots - 1);
     const Lds<D, W> sm(smem + slot * state_floats, G);
-    while (__hip_atomic_load(&s_epoch[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) !=
-           r_item)
+    for (int spin = 0; __hip_atomic_load(&s_epoch[slot], __ATOMIC_ACQUIRE,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP) != r_item; ++spin) {
+      if (spin == kSpinLimit) {
+        abort_wait();
+        return;
+      }
       __builtin_amdgcn_s_sleep(1);
+    }
     float ls = lsum;
     ls += shfl_xor_f(ls, 16);
     ls += shfl_xor_f(ls, 32);
+    // State index = the wave's lane in the item, so the merge below adds the
+    // partial states in an order fixed by logical positions.
     if (quad == 0) {
-      sm.m[w * kMaxGroup + g] = m;
-      sm.l[w * kMaxGroup + g] = ls;
+      sm.m[d.wr * kMaxGroup + g] = m;
+      sm.l[d.wr * kMaxGroup + g] = ls;
     }
     if (g < G) {
 #pragma unroll
       for (int i = 0; i < D / 16; ++i)
-        *reinterpret_cast<f32x4*>(&sm.acc[(w * G + g) * (D + 4) + i * 16 + quad * 4]) = acc[i];
+        *reinterpret_cast<f32x4*>(&sm.acc[(d.wr * G + g) * (D + 4) + i * 16 + quad * 4]) =
+            acc[i];
     }
     int before = 0;
     if (lane == 0)
@@ -621,6 +662,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         c[v] = (mv == kNegInf) ? 0.f : exp2_fast(mv - M);
         lam += sm.l[v * kMaxGroup + g] * c[v];
       }
+      // A whole sequence: scale by 1/lambda (one division per head).
+      const float inv = split ? 1.f : (lam > 0.f ? 1.f / lam : 0.f);
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -628,7 +671,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         for (int v = 0; v < W; ++v)
           val += *reinterpret_cast<const f32x4*>(&sm.acc[(v * G + g) * (D + 4) + i * 16 +
                                                          quad * 4]) * c[v];
-        if (!split) val = lam > 0.f ? val / lam : f32x4{0.f, 0.f, 0.f, 0.f};
+        val *= inv;
         *reinterpret_cast<f32x4*>(&rec[g * D + i * 16 + quad * 4]) = val;
       }
       if (quad == 0) {
@@ -675,8 +718,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   auto step = [&](Tile<D, BS>& tc, bf16x8* qc, bool hc, Tile<D, BS>& tn, bf16x8* qn,
                   bool& hn) -> bool {
     const bool last = k + 1 >= cur.npos;
+    if (last && !have_nxt) {
+      nxt = desc(r + 1);
+      have_nxt = true;
+    }
     load_pos(tn, qn, last ? nxt : cur, last ? 0 : k + 1, hn);
-    compute(tc, qc, hc ? cur.L - (cur.b0 + w + k * W) * BS : 0);
+    compute(tc, qc, hc ? cur.L - (cur.b0 + cur.wr + k * W) * BS : 0);
     if (!last) {
       ++k;
       return true;
@@ -689,7 +736,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     if (!nxt.valid) return false;
     ++r;
     cur = nxt;
-    nxt = desc(r + 1);
+    have_nxt = false;
     k = 0;
     return true;
   };
@@ -812,14 +859,18 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the partition states of split sequences, in
-// partition order: with M = max_p m_p, out = sum_p 2^(m_p - M) acc_p /
-// sum_p 2^(m_p - M) l_p.  One workgroup per (split sequence, KV head), four
-// features per thread.
+// partition order: a running (M, lambda, value) absorbs partition p as
+//   M' = max(M, m_p),  lambda' = lambda 2^(M - M') + l_p 2^(m_p - M'),
+//   value' = value 2^(M - M') + acc_p 2^(m_p - M'),   out = value / lambda.
+// The loads of a partition do not depend on the running state, so a batch of
+// partitions is fetched at once.  One workgroup per (split sequence, KV
+// head) at a time, four features per thread.
 // ---------------------------------------------------------------------------
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits(DecodeParams a) {
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+  constexpr int kBatch = 4;
   const int Hkv = a.num_kv_heads, G = a.group;
   const int total = a.ws_ctrl[kCtrlSplits] * Hkv;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -830,16 +881,28 @@ __global__ __launch_bounds__(256) void merge_splits(DecodeParams a) {
     for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
       const int g = idx / (D / 4);
       const int d4 = idx - g * (D / 4);
-      float M = kNegInf;
-      for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_ml[((prow + p) * G + g) * 2]);
-      float lam = 0.f;
+      float M = kNegInf, lam = 0.f;
       f4 val = {0.f, 0.f, 0.f, 0.f};
-      for (int p = 0; p < nparts; ++p) {
-        const int64_t row = (prow + p) * G + g;
-        const float mp = a.ws_ml[row * 2];
-        const float c = (mp == kNegInf) ? 0.f : exp2_fast(mp - M);
-        lam += a.ws_ml[row * 2 + 1] * c;
-        val += *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4) * c;
+      for (int p0 = 0; p0 < nparts; p0 += kBatch) {
+        float mp[kBatch], lp[kBatch];
+        f4 ap[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int64_t row = (prow + min(p0 + j, nparts - 1)) * G + g;
+          mp[j] = a.ws_ml[row * 2];
+          lp[j] = a.ws_ml[row * 2 + 1];
+          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (p0 + j >= nparts) break;
+          const float Mn = fmaxf(M, mp[j]);
+          if (Mn == kNegInf) continue;        // nothing live yet
+          const float cold = exp2_fast(M - Mn), cnew = exp2_fast(mp[j] - Mn);
+          lam = lam * cold + lp[j] * cnew;
+          val = val * cold + ap[j] * cnew;
+          M = Mn;
+        }
       }
       const f4 o = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) = o;
@@ -859,11 +922,12 @@ size_t smem_bytes(int group, bool valu, int block_size, int lds_slots, int lds_r
 }
 
 // LDS of the matrix-core kernel: two state slots and as many output records
-// (up to kMaxLdsRecords) as keep it within 74 KB, so that two workgroups fit
-// in one CU's 160 KB; a single slot when two slots and one record do not fit.
+// (up to kMaxLdsRecords) as fit in this workgroup's share of the CU's 160 KB
+// (8 waves per CU at the kernel's register use: 148 KB * W / 8); a single
+// slot when two slots and one record do not fit.
 template <int D>
 void lds_layout_for(int group, int* slots, int* records) {
-  const int budget = 74 * 1024 / 4;
+  const int budget = 148 * 1024 / 4 * kWaves / 8;
   const int state = lds_state_floats<D, kWaves>(group);
   const int rec = lds_record_floats<D>(group);
   int ns = 2;
@@ -901,6 +965,9 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   size_t smem;
   DecodeParams p = p0;
   lds_layout_for<D>(p0.group, &p.lds_slots, &p.lds_records);
+  // The adaptive partition keeps one partition at most 2/W of a workgroup's
+  // share, so each wave's part of it is at most half a wave's share.
+  if (p.balance) p.balance = kWaves / 2;
   if (type == KvType::BF16 && !vector_alu) {
     kernel = (const void*)decode_mfma_bf16<D, BS, kWaves>;
     smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
@@ -931,7 +998,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   e = hipGetLastError();
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
-  const unsigned mgrid = (unsigned)(pairs < 2048 ? pairs : 2048);
+  const unsigned mgrid = (unsigned)(pairs < 256 ? pairs : 256);
   hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -28,7 +28,8 @@ struct DecodeParams {
   int32_t part_blocks_max;    // largest partition the planner may pick
   int32_t num_parts_max;      // ceil(max_blocks / part_blocks_min): partition-state row stride
   int32_t balance;            // planner: the largest item is at most 1/balance of a
-                              // workgroup's share of the work (0: always part_blocks_min)
+                              // workgroup's share of the work (0: always part_blocks_min;
+                              // the API sets 1 for adaptive, the launcher the ratio)
   int32_t decode_grid;        // workgroups of the decode launch (set by the launcher)
   int32_t lds_slots;          // LDS state slots of the matrix-core kernel (set by the launcher)
   int32_t lds_records;        // LDS output records of the matrix-core kernel (set by the launcher)
@@ -44,7 +45,11 @@ struct DecodeParams {
 constexpr int kCtrlEntries = 0;
 constexpr int kCtrlPartBlocks = 1;
 constexpr int kCtrlSplits = 2;
-constexpr int kCtrlSize = 4;
+// Set by the decode kernel if one of its waits on other waves of its
+// workgroup did not end (a broken invariant; the output is then incomplete).
+// Tests read it; cleared by the planner.
+constexpr int kCtrlAbort = 20;
+constexpr int kCtrlSize = 32;
 
 enum class KvType { F32 = 0, BF16 = 1 };
 

@@ -42,6 +42,18 @@ def _case(cfg, poison="nan", block_size=None, long_last=False, num_seqs=None):
     return w, k_ref, v_ref, ref
 
 
+# Word of the decode workspace where the kernel records a wait between its
+# waves that did not end (it then gives up rather than hang).
+_CTRL_ABORT_WORD = 20
+
+
+def _assert_no_abort():
+    import torch
+    import paged_kv_cache_349_amd as pa
+    for ws in pa._workspaces.values():
+        assert int(ws[:128].view(torch.int32)[_CTRL_ABORT_WORD]) == 0, "decode kernel gave up a wait"
+
+
 def _run(w, **decode_kw):
     import torch
     import paged_kv_cache_349_amd as pa
@@ -51,6 +63,7 @@ def _run(w, **decode_kw):
     pa.decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(w.scale),
               w.block_size, **decode_kw)
     torch.cuda.synchronize()
+    _assert_no_abort()
     return d
 
 
