@@ -149,6 +149,21 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_blocks_per_seq, int32_t block_size);
 
+/*
+ * Kernel timing, for benchmarks and diagnostics.  Between
+ * pa_kernel_timing_begin and pa_kernel_timing_end, each of the first
+ * `capacity` pa_decode / pa_decode_ex calls made on the device that was
+ * current at begin records a pair of HIP events on its stream, right before
+ * and right after its attention kernel (the planner and the partition merge
+ * are outside the pair).  pa_kernel_timing_end waits for those events (it
+ * synchronises), writes the summed elapsed milliseconds and the number of
+ * timed calls, and releases the events.  Begin creates the events (host API
+ * objects, no caller buffer); timing is process-wide and not nested: begin
+ * while on, or end while off, is PA_ERR_INVALID_ARG.
+ */
+int pa_kernel_timing_begin(int32_t capacity);
+int pa_kernel_timing_end(double* total_ms, int32_t* launches);
+
 /* Static description of a status code. */
 const char* pa_status_string(int32_t status);
 

@@ -42,6 +42,9 @@ _SIGNATURES = {
                   [_vp, ctypes.c_size_t, _vp]),
     "pa_decode_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float] + [_c_int] * 8 +
                      [_vp, ctypes.c_size_t, _c_int, _c_int, _vp]),
+    "pa_kernel_timing_begin": (ctypes.c_int, [_c_int]),
+    "pa_kernel_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(_c_int)]),
     "pa_status_string": (ctypes.c_char_p, [_c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
@@ -184,5 +187,18 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     return out
 
 
+def kernel_timing_begin(capacity: int):
+    """Time the attention kernel of the next `capacity` decode calls (see the C header)."""
+    _check(load_library().pa_kernel_timing_begin(int(capacity)))
+
+
+def kernel_timing_end():
+    """Wait for the timed kernels; returns (total milliseconds, number of timed calls)."""
+    ms = ctypes.c_double(0.0)
+    n = _c_int(0)
+    _check(load_library().pa_kernel_timing_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
 __all__ = ["write_kv", "decode", "workspace_bytes", "load_library", "LIB_PATH",
-           "PagedAttentionError"]
+           "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]

@@ -8,6 +8,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -76,6 +79,37 @@ Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
   }
   l.total = off;
   return l;
+}
+
+// Event pairs handed to the decode launcher while kernel timing is on.
+struct KernelTiming {
+  std::mutex mu;
+  bool on = false;
+  int device = -1;
+  size_t used = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+
+  void release() {
+    for (auto& ev : events) {
+      hipEventDestroy(ev.first);
+      hipEventDestroy(ev.second);
+    }
+    events.clear();
+    used = 0;
+    on = false;
+  }
+};
+
+KernelTiming g_timing;
+
+// The next unused event pair if timing is on for the current device.
+std::pair<hipEvent_t, hipEvent_t> next_timing_events() {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  int dev = -1;
+  if (!g_timing.on || g_timing.used >= g_timing.events.size() || hipGetDevice(&dev) != hipSuccess ||
+      dev != g_timing.device)
+    return {nullptr, nullptr};
+  return g_timing.events[g_timing.used++];
 }
 
 bool shapes_valid(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -224,8 +258,10 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
   p.ws_split = (int2*)(ws + lay.split_off);
   p.ws_acc = lay.num_parts_max > 1 ? (float*)(ws + lay.acc_off) : nullptr;
   p.ws_ml = lay.num_parts_max > 1 ? (float*)(ws + lay.ml_off) : nullptr;
+  const auto ev = next_timing_events();
   hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
-                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream);
+                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream,
+                                   ev.first, ev.second);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -238,6 +274,55 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
   return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                       num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int pa_kernel_timing_begin(int32_t capacity) {
+  if (capacity <= 0 || capacity > (1 << 20))
+    return fail(PA_ERR_INVALID_ARG, "capacity=%d is not in [1, 2^20]", capacity);
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (g_timing.on) return fail(PA_ERR_INVALID_ARG, "kernel timing is already on");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  g_timing.events.reserve((size_t)capacity);
+  for (int32_t i = 0; i < capacity; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    e = hipEventCreate(&a);
+    if (e == hipSuccess) {
+      e = hipEventCreate(&b);
+      if (e != hipSuccess) hipEventDestroy(a);
+    }
+    if (e != hipSuccess) {
+      g_timing.release();
+      return fail(PA_ERR_LAUNCH, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    g_timing.events.emplace_back(a, b);
+  }
+  g_timing.device = dev;
+  g_timing.used = 0;
+  g_timing.on = true;
+  return ok();
+}
+
+int pa_kernel_timing_end(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(PA_ERR_INVALID_ARG, "null output pointer");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (!g_timing.on) return fail(PA_ERR_INVALID_ARG, "kernel timing is not on");
+  double sum = 0.0;
+  hipError_t e = hipSuccess;
+  for (size_t i = 0; i < g_timing.used && e == hipSuccess; ++i) {
+    float ms = 0.0f;
+    e = hipEventSynchronize(g_timing.events[i].second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timing.events[i].first,
+                                                 g_timing.events[i].second);
+    sum += ms;
+  }
+  const size_t used = g_timing.used;
+  g_timing.release();
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "kernel timing events: %s", hipGetErrorString(e));
+  *total_ms = sum;
+  *launches = (int32_t)used;
+  return ok();
 }
 
 }  // extern "C"

@@ -959,7 +959,7 @@ int resident_workgroups(const void* kernel, int threads, size_t smem) {
 
 template <int D, int BS>
 hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_alu,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
   const int threads = 64 * kWaves;
   const void* kernel;
   size_t smem;
@@ -986,6 +986,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
   if (type == KvType::BF16 && !vector_alu)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),
                        smem, stream, p);
@@ -996,7 +997,9 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
     hipLaunchKernelGGL((decode_valu<float, D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),
                        smem, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess || p.num_parts_max <= 1) return e;
+  if (e != hipSuccess) return e;
+  if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
+  if (p.num_parts_max <= 1) return hipSuccess;
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
   const unsigned mgrid = (unsigned)(pairs < 256 ? pairs : 256);
   hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p);
@@ -1012,15 +1015,16 @@ bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t
 }
 
 hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
-                         int32_t block_size, bool vector_alu, hipStream_t stream) {
+                         int32_t block_size, bool vector_alu, hipStream_t stream,
+                         hipEvent_t ev_before, hipEvent_t ev_after) {
   if (head_dim == 64 && block_size == 16)
-    return launch_decode_shape<64, 16>(p, type, vector_alu, stream);
+    return launch_decode_shape<64, 16>(p, type, vector_alu, stream, ev_before, ev_after);
   if (head_dim == 64 && block_size == 32)
-    return launch_decode_shape<64, 32>(p, type, vector_alu, stream);
+    return launch_decode_shape<64, 32>(p, type, vector_alu, stream, ev_before, ev_after);
   if (head_dim == 128 && block_size == 16)
-    return launch_decode_shape<128, 16>(p, type, vector_alu, stream);
+    return launch_decode_shape<128, 16>(p, type, vector_alu, stream, ev_before, ev_after);
   if (head_dim == 128 && block_size == 32)
-    return launch_decode_shape<128, 32>(p, type, vector_alu, stream);
+    return launch_decode_shape<128, 32>(p, type, vector_alu, stream, ev_before, ev_after);
   return hipErrorInvalidValue;
 }
 

@@ -59,8 +59,11 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            KvType type, hipStream_t stream);
 
 // Returns hipErrorInvalidValue for a (type, D, BS) combination without a kernel.
+// Non-null events are recorded on `stream` right before and right after the
+// attention kernel (not the planner or the merge), for kernel timing.
 hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
-                         int32_t block_size, bool vector_alu, hipStream_t stream);
+                         int32_t block_size, bool vector_alu, hipStream_t stream,
+                         hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
 
 bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t group);
 

@@ -140,3 +140,12 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(pa, "_lib", None)
     with pytest.raises(RuntimeError):
         pa.load_library(str(tmp_path / "missing.so"))
+
+
+def test_kernel_timing_argument_errors(lib):
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    assert lib.pa_kernel_timing_begin(0) == 1
+    assert lib.pa_kernel_timing_begin(-3) == 1
+    assert lib.pa_kernel_timing_end(ctypes.byref(ms), ctypes.byref(n)) == 1   # not on
+    assert lib.pa_kernel_timing_end(None, ctypes.byref(n)) == 1

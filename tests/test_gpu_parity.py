@@ -218,3 +218,19 @@ def test_bit_exact_write_of_nan_payloads():
         torch.cuda.synchronize()
         assert np.array_equal(_raw(torch_to_np(d.k_cache, dt)), _raw(k_ref))
         assert np.array_equal(_raw(torch_to_np(d.v_cache, dt)), _raw(v_ref))
+
+
+def test_kernel_timing_events():
+    """Kernel timing records one event pair per decode call, up to its capacity."""
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    w = _custom([300, 17, 1000], 8, 4, 128, 16, "bf16", seed=5)
+    d = upload(w)
+    pa.kernel_timing_begin(2)
+    for _ in range(3):
+        pa.decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                  float(w.scale), 16)
+    ms, n = pa.kernel_timing_end()
+    assert n == 2 and ms > 0.0
+    with pytest.raises(ValueError):
+        pa.kernel_timing_end()
