@@ -1,6 +1,7 @@
 // C ABI of libpa.so: argument checks, partition choice, dispatch.
 // The declarations and the contract live in include/paged_attention.h.
 #include "paged_attention.h"
+#include "block_manager.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -15,8 +16,10 @@
 #include "pa_internal.h"
 
 namespace {
-
 thread_local char g_last_error[512];
+}  // namespace
+
+namespace pa {
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -26,10 +29,17 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+int succeed() {
   g_last_error[0] = '\0';
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+int ok() { return pa::succeed(); }
 
 constexpr double kLog2e = 1.4426950408889634;
 
@@ -129,6 +139,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype/shape combination";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_NO_ROOM: return "no room in the block pool";
     default: return "unknown status";
   }
 }

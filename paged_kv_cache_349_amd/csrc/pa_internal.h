@@ -53,6 +53,11 @@ constexpr int kCtrlSize = 32;
 
 enum class KvType { F32 = 0, BF16 = 1 };
 
+// Status helpers shared by the C entry points: fail() stores the message for
+// pa_last_error() (thread-local) and returns `code`; succeed() clears it.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int succeed();
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t num_tokens, int32_t num_blocks,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -75,11 +75,11 @@ def pin_pages_example(factory):
         assert slots[pos] == slot, (pos, slots[pos], slot)
     # the sketch's free list is list(range(total)) taken from the front
     m = factory(1000, 0, 16, 64)
-    m.add("a", 0)
-    m.add("b", 0)
+    m.add(10, 0)
+    m.add(11, 0)
     got = []
     for _ in range(33):
-        got.append((m.append("a")[0] // 16, m.append("b")[0] // 16))
+        got.append((m.append(10)[0] // 16, m.append(11)[0] // 16))
     assert got[0] == (0, 1) and got[16] == (2, 3) and got[32] == (4, 5), got
     # the allocation trigger: blocks open at lengths 1, bs+1, 2bs+1, ...
     for bsz, lengths in opens:
