@@ -74,6 +74,84 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+PCIE_GEN5_X16_GBPS = 63.0   # 32 GT/s x 16 lanes, 128b/130b coding, per direction
+
+
+def bench_blocks(args, w, d, dev, stream):
+    """Block manager, copy-on-write copies and swap on the same workload.
+
+    Runs last: the copies overwrite blocks of the decode pool.
+      kv_waste        contiguous max-context reservation vs the manager's paged
+                      allocation of this workload's sequences
+      manager_us      host time of the manager's work for one decode step
+                      (one batched append for all sequences + their tables)
+      copy            pa_copy_blocks of 4096 random block pairs (32 KB per K or
+                      V span): bytes read + written per launch / mean duration
+      swap_out/in     pa_swap_blocks of 2048 blocks to / from a pinned host
+                      pool, against one contiguous copy of the same bytes
+                      (torch / HIP DMA) and the host link's nominal rate
+    """
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd import waste
+
+    out = {}
+    cfg = args.config
+    wr = waste.waste(cfg, w.block_size)
+    out["kv_waste"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in wr.items()}
+    out["manager_us_per_step"] = round(waste.time_step(cfg, w.block_size), 2)
+
+    rng = np.random.default_rng(1)
+    NB = w.num_blocks
+    span = w.num_kv_heads * w.block_size * w.head_dim * 2
+    n = min(4096, NB // 2)
+    ids = rng.permutation(NB)[:2 * n].astype(np.int32)
+    src = torch.from_numpy(ids[:n]).to(dev)
+    dst = torch.from_numpy(ids[n:]).to(dev)
+
+    def timed(fn, iters=20):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    us = timed(lambda: pa.copy_blocks(d.k_cache, d.v_cache, src, dst))
+    moved = 2 * n * span * 2
+    out["copy"] = {"pairs": n, "bytes_per_launch": moved, "us_mean": round(us, 2),
+                   "achieved_gbps": round(moved / (us * 1e-6) / 1e9, 1),
+                   "peak_gbps": HBM_PEAK_GBPS}
+    log(f"copy_blocks: {n} pairs, {us:.1f} us, {moved / (us * 1e-6) / 1e9:.0f} GB/s")
+
+    ns = min(2048, NB)
+    hk = torch.empty((ns,) + tuple(d.k_cache.shape[1:]), dtype=d.k_cache.dtype, pin_memory=True)
+    hv = torch.empty((ns,) + tuple(d.v_cache.shape[1:]), dtype=d.v_cache.dtype, pin_memory=True)
+    dev_ids = torch.from_numpy(rng.permutation(NB)[:ns].astype(np.int32)).to(dev)
+    host_ids = torch.from_numpy(rng.permutation(ns).astype(np.int32)).to(dev)
+    t_out = timed(lambda: pa.swap_blocks(hk, hv, d.k_cache, d.v_cache, dev_ids, host_ids), 5)
+    t_in = timed(lambda: pa.swap_blocks(d.k_cache, d.v_cache, hk, hv, host_ids, dev_ids), 5)
+    sb = 2 * ns * span
+    flat_d = torch.empty(sb, dtype=torch.uint8, device=dev)
+    flat_h = torch.empty(sb, dtype=torch.uint8, pin_memory=True)
+    t_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), 5)
+    t_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), 5)
+    gb = lambda t: round(sb / (t * 1e-6) / 1e9, 2)
+    out["swap"] = {"blocks": ns, "bytes": sb, "out_us": round(t_out, 1), "in_us": round(t_in, 1),
+                   "out_gbps": gb(t_out), "in_gbps": gb(t_in),
+                   "contiguous_copy_gbps": {"d2h": gb(t_d2h), "h2d": gb(t_h2d)},
+                   "link_peak_gbps": PCIE_GEN5_X16_GBPS}
+    log(f"swap_blocks: {ns} blocks, out {gb(t_out)} GB/s, in {gb(t_in)} GB/s "
+        f"(contiguous copy d2h {gb(t_d2h)}, h2d {gb(t_h2d)})")
+    return out
+
+
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -92,6 +170,8 @@ def parse_args():
                    help="decode launches timed after flushing the caches (0 = skip)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--no-blocks", action="store_true",
+                   help="skip the block-manager, copy-on-write and swap measurements")
     return p.parse_args()
 
 
@@ -260,6 +340,9 @@ def main() -> int:
         b.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: one 1 GiB device copy done")
+
+    if not args.no_blocks:
+        result["blocks"] = bench_blocks(args, w, d, dev, stream)
 
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits

@@ -86,6 +86,46 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
                 void* stream);
 
 /*
+ * Copy-on-write block copies inside one pool.  For i in [0, num_pairs):
+ *   block dst_blocks[i] := block src_blocks[i]
+ * in both k_cache and v_cache (all KV heads, all block_size positions; raw
+ * bits).  This is the copy a writer needs before it appends into a block that
+ * other sequences share ("Paged Attention: OS-Inspired Memory Management for
+ * KV Caches", section "Key terms in this lesson": copy-on-write gives the
+ * writer a private copy; "How does vLLM PagedAttention manage Virtual Memory
+ * Pages ...", section "Key Technical Innovations", item 3).  The pairs come
+ * from the block manager's pa_bm_append.
+ *   src_blocks, dst_blocks  [num_pairs] int32, device (or device-visible
+ *                           pinned host memory)
+ * A pair with an id outside [0, num_blocks) is skipped.  Destinations must be
+ * distinct and must not be sources in the same call (else the copies race).
+ * num_pairs == 0 is a successful no-op.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, int32_t num_pairs, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                   void* stream);
+
+/*
+ * Block swap between two pools of the same block shape, e.g. the device pool
+ * and a host pool in pinned memory (hipHostMalloc, which the device
+ * addresses directly), for preemption by swapping ("PagedAttention and KV
+ * memory management", section "Key takeaways").  For i in [0, num_pairs):
+ *   dst pool block dst_blocks[i] := src pool block src_blocks[i]
+ * in both tensors (raw bits).  The pairs come from pa_bm_swap_out (device ->
+ * host) or pa_bm_swap_in (host -> device).  Pools and id arrays must be
+ * addressable by the device; a pinned host pool is read or written across the
+ * host link by the kernel itself (one launch for all pairs).  A pair with an
+ * id outside its pool is skipped; destinations must be distinct and, when
+ * both sides are the same pool, not sources of the same call.  Completion is
+ * ordered by `stream`: the host must synchronise before it reads a host pool.
+ */
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t kv_dtype, void* stream);
+
+/*
  * Bytes of device workspace pa_decode needs for these shapes (an invalid
  * shape returns 0).  The workspace holds the call's work list, its counters
  * and the softmax states (max, sum, weighted sum) of context partitions that

@@ -7,6 +7,8 @@ raises.
 
     write_kv(k_cache, v_cache, k_new, v_new, slot_mapping)
     decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size)
+    copy_blocks(k_cache, v_cache, src_blocks, dst_blocks)           # copy-on-write
+    swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks)   # device <-> pinned host
 
 Layouts: k_cache [NB, Hkv, bs, D], v_cache [NB, Hkv, D, bs] (float32 or
 bfloat16); q [S, Hq, D] and k_new/v_new [T, Hkv, D] in the cache dtype;
@@ -35,6 +37,8 @@ _vp = ctypes.c_void_p
 _SIGNATURES = {
     "pa_write_kv": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _vp]),
+    "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp]),
+    "pa_swap_blocks": (ctypes.c_int, [_vp] * 6 + [_c_int] * 7 + [_vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 7),
     "pa_decode_workspace_bytes_ex": (ctypes.c_size_t, [_c_int] * 8),
     "pa_decode_partition_tokens": (_c_int, [_c_int] * 4),
@@ -132,6 +136,60 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
                            _dtype_code(k_cache), _stream_handle(dev, stream)))
 
 
+def _pool_shape(k, v):
+    _need(k.dim() == 4 and v.dim() == 4, "caches must be 4-D")
+    NB, Hkv, bs, D = k.shape
+    _need(tuple(v.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(k.dtype == v.dtype, "k and v caches must share a dtype")
+    return NB, Hkv, bs, D
+
+
+def _ids_pair(src, dst):
+    torch = _torch()
+    _need(src.dtype == torch.int32 and dst.dtype == torch.int32 and src.dim() == 1 and
+          src.shape == dst.shape, "block id lists: int32 [n], equal lengths")
+    return src.shape[0]
+
+
+def copy_blocks(k_cache, v_cache, src_blocks, dst_blocks, stream=None):
+    """Copy-on-write: block dst_blocks[i] := block src_blocks[i] in both caches (raw bits)."""
+    lib = load_library()
+    dev = _on_gpu(k_cache, v_cache, src_blocks, dst_blocks)
+    NB, Hkv, bs, D = _pool_shape(k_cache, v_cache)
+    n = _ids_pair(src_blocks, dst_blocks)
+    _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_blocks.data_ptr(),
+                              dst_blocks.data_ptr(), n, NB, Hkv, D, bs, _dtype_code(k_cache),
+                              _stream_handle(dev, stream)))
+
+
+def _device_visible(*ts):
+    dev = None
+    for t in ts:
+        _need(t.is_contiguous(), "all tensors must be contiguous")
+        if t.is_cuda:
+            _need(dev is None or t.device == dev, "device tensors must share one GPU")
+            dev = t.device
+        else:
+            _need(t.is_pinned(), "host tensors must be in pinned memory")
+    _need(dev is not None, "at least one tensor must be on the GPU")
+    return dev
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks, stream=None):
+    """dst pool block dst_blocks[i] := src pool block src_blocks[i]; pools on the GPU or pinned."""
+    lib = load_library()
+    dev = _device_visible(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks)
+    SNB, Hkv, bs, D = _pool_shape(src_k, src_v)
+    DNB, Hkv2, bs2, D2 = _pool_shape(dst_k, dst_v)
+    _need((Hkv, bs, D) == (Hkv2, bs2, D2) and src_k.dtype == dst_k.dtype,
+          "pools must share block shape and dtype")
+    n = _ids_pair(src_blocks, dst_blocks)
+    _check(lib.pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(),
+                              src_v.data_ptr(), src_blocks.data_ptr(), dst_blocks.data_ptr(), n,
+                              SNB, DNB, Hkv, D, bs, _dtype_code(src_k),
+                              _stream_handle(dev, stream)))
+
+
 def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, block_size,
                     kv_dtype_code, partition_tokens=0) -> int:
     return int(load_library().pa_decode_workspace_bytes_ex(
@@ -200,5 +258,5 @@ def kernel_timing_end():
     return ms.value, n.value
 
 
-__all__ = ["write_kv", "decode", "workspace_bytes", "load_library", "LIB_PATH",
-           "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]
+__all__ = ["write_kv", "decode", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+           "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]

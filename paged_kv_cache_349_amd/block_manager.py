@@ -77,10 +77,14 @@ def _call(status):
 
 
 def _ptr(a):
-    return a.ctypes.data_as(_vp) if a is not None and a.size else None
+    # the buffer's address as an int (ctypes passes it as a void*)
+    return a.__array_interface__["data"][0] if a is not None and a.size else None
 
 
 def _ids(seqs):
+    if isinstance(seqs, np.ndarray) and seqs.dtype == np.int64 and seqs.ndim == 1 and \
+            seqs.flags.c_contiguous:
+        return seqs
     return np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
 
 
@@ -115,16 +119,25 @@ class BlockManager:
         _call(_lib().pa_bm_add(self._h, int(seq), int(num_tokens), _ptr(slots)))
         return slots
 
-    def append_batch(self, seqs):
+    def append_batch(self, seqs, out=None):
+        """One token for each listed sequence: (slots, cow_src, cow_dst).
+
+        out: optional (slots, src, dst) int32 arrays of at least len(seqs)
+        entries to write into (e.g. pinned staging buffers); the returned
+        arrays are then views of them.
+        """
         ids = _ids(seqs)
         n = ids.size
-        slots = np.empty(n, np.int32)
-        src = np.empty(n, np.int32)
-        dst = np.empty(n, np.int32)
+        if out is None:
+            out = (np.empty(n, np.int32), np.empty(n, np.int32), np.empty(n, np.int32))
+        slots, src, dst = out
+        if min(slots.size, src.size, dst.size) < n or not all(
+                a.dtype == np.int32 and a.flags.c_contiguous for a in out):
+            raise ValueError("out arrays: contiguous int32 with room for every sequence")
         nc = _i32(0)
         _call(_lib().pa_bm_append(self._h, _ptr(ids), n, _ptr(slots), _ptr(src), _ptr(dst),
                                   ctypes.byref(nc)))
-        return slots, src[:nc.value].copy(), dst[:nc.value].copy()
+        return slots[:n], src[:nc.value], dst[:nc.value]
 
     def append(self, seq):
         """One token for one sequence: (slot, cow_src, cow_dst), -1 when nothing to copy."""
@@ -155,11 +168,16 @@ class BlockManager:
         return self._swap(_lib().pa_bm_swap_in, seqs)
 
     # -- queries -----------------------------------------------------------
-    def tables(self, seqs, stride=None):
+    def tables(self, seqs, stride=None, out=None):
+        """Block tables [n, stride] (-1 padded) and lengths [n]; out=(tables, lens) to reuse."""
         ids = _ids(seqs)
         stride = self.max_blocks if stride is None else int(stride)
-        t = np.empty((ids.size, stride), np.int32)
-        lens = np.empty(ids.size, np.int32)
+        if out is None:
+            out = (np.empty((ids.size, stride), np.int32), np.empty(ids.size, np.int32))
+        t, lens = out
+        if t.shape != (ids.size, stride) or lens.shape != (ids.size,) or \
+                t.dtype != np.int32 or lens.dtype != np.int32 or not t.flags.c_contiguous:
+            raise ValueError("out arrays: int32 [n, stride] and [n]")
         _call(_lib().pa_bm_block_tables(self._h, _ptr(ids), ids.size, _ptr(t), stride, _ptr(lens)))
         return t, lens
 

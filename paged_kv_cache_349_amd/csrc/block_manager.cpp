@@ -72,6 +72,7 @@ struct pa_block_manager {
   std::unordered_map<int64_t, Seq> seqs;
   uint64_t stamp = 0;
   std::unordered_map<int32_t, int32_t> scratch;   // per-call block -> count / mapping
+  std::vector<Seq*> batch;                          // per-call sequences, in list order
 
   Seq* find(int64_t id) {
     auto it = seqs.find(id);
@@ -92,10 +93,12 @@ using pa::fail;
 using pa::succeed;
 
 // Checks shared by the batch calls: every id known, in `pool`, listed once.
+// Leaves the sequences in bm->batch (map values do not move on insertion).
 int check_batch(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t pool) {
   if (n < 0) return fail(PA_ERR_INVALID_ARG, "n=%d < 0", n);
   if (n > 0 && !seqs) return fail(PA_ERR_INVALID_ARG, "null sequence list");
   const uint64_t stamp = ++bm->stamp;
+  bm->batch.clear();
   for (int32_t i = 0; i < n; ++i) {
     Seq* s = bm->find(seqs[i]);
     if (!s) return fail(PA_ERR_INVALID_ARG, "unknown sequence %lld", (long long)seqs[i]);
@@ -105,6 +108,7 @@ int check_batch(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t po
     if (s->stamp == stamp)
       return fail(PA_ERR_INVALID_ARG, "sequence %lld listed twice", (long long)seqs[i]);
     s->stamp = stamp;
+    bm->batch.push_back(s);
   }
   return PA_OK;
 }
@@ -118,8 +122,8 @@ int swap(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t from, int
   auto& first = bm->scratch;
   first.clear();
   int32_t distinct = 0;
-  for (int32_t i = 0; i < n; ++i)
-    for (int32_t b : bm->find(seqs[i])->table)
+  for (Seq* s : bm->batch)
+    for (int32_t b : s->table)
       if (first.emplace(b, distinct).second) ++distinct;
   if (distinct > capacity || (distinct > 0 && (!src_blocks || !dst_blocks)))
     return fail(PA_ERR_INVALID_ARG, "pair arrays hold %d entries, %d needed", capacity, distinct);
@@ -131,8 +135,7 @@ int swap(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t from, int
   // Map each distinct block once; count the references that move.
   std::vector<int32_t> moved((size_t)distinct, 0);
   for (int32_t k = 0; k < distinct; ++k) dst_blocks[k] = -1;
-  for (int32_t i = 0; i < n; ++i) {
-    Seq* s = bm->find(seqs[i]);
+  for (Seq* s : bm->batch) {
     for (int32_t& b : s->table) {
       const int32_t k = first[b];
       if (dst_blocks[k] < 0) {
@@ -236,10 +239,10 @@ int pa_bm_append(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t* 
   // Dry run: blocks needed, counting the references that earlier entries of
   // this batch drop from a shared last block (its last holder writes in place).
   auto& dropped = bm->scratch;
-  dropped.clear();
+  if (!dropped.empty()) dropped.clear();
   int32_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const Seq* s = bm->find(seqs[i]);
+    const Seq* s = bm->batch[(size_t)i];
     const int32_t j = s->len / bs;
     if (s->len % bs == 0) {
       if (j >= bm->max_blocks)
@@ -260,7 +263,7 @@ int pa_bm_append(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t* 
     return fail(PA_ERR_NO_ROOM, "no room: %d blocks needed, %d free", need, dev.free.size());
   int32_t ncow = 0;
   for (int32_t i = 0; i < n; ++i) {
-    Seq* s = bm->find(seqs[i]);
+    Seq* s = bm->batch[(size_t)i];
     const int32_t j = s->len / bs, o = s->len % bs;
     if (o == 0) {
       s->table.push_back(dev.take());

@@ -168,6 +168,48 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
   return ok();
 }
 
+static int copy_blocks_common(const char* what, void* dst_k, void* dst_v, const void* src_k,
+                              const void* src_v, const int32_t* src_ids, const int32_t* dst_ids,
+                              int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t kv_dtype, void* stream) {
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs=%d < 0", what, num_pairs);
+  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: kv_dtype=%d is neither F32 nor BF16", what, kv_dtype);
+  if (src_blocks <= 0 || dst_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: sizes must be positive (blocks %d/%d num_kv_heads=%d head_dim=%d "
+                "block_size=%d)",
+                what, src_blocks, dst_blocks, num_kv_heads, head_dim, block_size);
+  if (num_pairs == 0) return ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !src_ids || !dst_ids)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer with num_pairs=%d", what, num_pairs);
+  const int64_t span = (int64_t)num_kv_heads * head_dim * block_size *
+                       (kv_dtype == PA_DTYPE_BF16 ? 2 : 4);
+  hipError_t e = pa::launch_copy_blocks(dst_k, dst_v, src_k, src_v, src_ids, dst_ids, num_pairs,
+                                        src_blocks, dst_blocks, span, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, int32_t num_pairs, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                   void* stream) {
+  return copy_blocks_common("copy_blocks", k_cache, v_cache, k_cache, v_cache, src_blocks,
+                            dst_blocks, num_pairs, num_blocks, num_blocks, num_kv_heads, head_dim,
+                            block_size, kv_dtype, stream);
+}
+
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs,
+                   int32_t src_num_blocks, int32_t dst_num_blocks, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t kv_dtype, void* stream) {
+  return copy_blocks_common("swap_blocks", dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks,
+                            num_pairs, src_num_blocks, dst_num_blocks, num_kv_heads, head_dim,
+                            block_size, kv_dtype, stream);
+}
+
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_blocks_per_seq, int32_t block_size) {
   if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 0;

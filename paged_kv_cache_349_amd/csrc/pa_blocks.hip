@@ -1,0 +1,82 @@
+// Whole-block copies between pools: copy-on-write inside the device pool and
+// swap between the device pool and a host pool.
+//
+// A block is one contiguous span in each cache tensor (all KV heads of
+// block_size tokens), so a pair (src, dst) is two span copies, one in the K
+// tensor and one in the V tensor.  Each workgroup copies one chunk of one
+// span; the grid is (chunks per span, pairs, 2 tensors).  The pair's ids are
+// read once per workgroup and made wave-uniform.  Either pool may be pinned
+// host memory that the device can address (hipHostMalloc): the same loads and
+// stores then travel over the host link.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;   // 16-byte vectors in flight per thread
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    char* __restrict__ dst_k, char* __restrict__ dst_v, const char* __restrict__ src_k,
+    const char* __restrict__ src_v, const int32_t* __restrict__ src_ids,
+    const int32_t* __restrict__ dst_ids, int32_t src_blocks, int32_t dst_blocks,
+    int64_t span_bytes) {
+  const int pair = blockIdx.y;
+  const int32_t s = __builtin_amdgcn_readfirstlane(src_ids[pair]);
+  const int32_t d = __builtin_amdgcn_readfirstlane(dst_ids[pair]);
+  if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
+  const char* from = (blockIdx.z == 0 ? src_k : src_v) + (int64_t)s * span_bytes;
+  char* to = (blockIdx.z == 0 ? dst_k : dst_v) + (int64_t)d * span_bytes;
+  const int64_t n = span_bytes / (int64_t)sizeof(V);
+  const int64_t chunk = (int64_t)kThreads * kUnroll;
+  const int64_t base = (int64_t)blockIdx.x * chunk + threadIdx.x;
+  const V* f = reinterpret_cast<const V*>(from);
+  V* t = reinterpret_cast<V*>(to);
+  V buf[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n) buf[u] = f[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n) t[i] = buf[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* src_ids, const int32_t* dst_ids, int32_t num_pairs,
+                              int32_t src_blocks, int32_t dst_blocks, int64_t span_bytes,
+                              hipStream_t stream) {
+  const bool wide = span_bytes % 16 == 0 &&
+                    (((uintptr_t)dst_k | (uintptr_t)dst_v | (uintptr_t)src_k | (uintptr_t)src_v) %
+                     16) == 0;
+  const int64_t elem = wide ? 16 : 2;
+  const int64_t n = span_bytes / elem;
+  const int64_t chunks = (n + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  if (chunks > INT32_MAX) return hipErrorInvalidValue;
+  // The pair index is the grid's y dimension, at most 65535 per launch.
+  for (int32_t off = 0; off < num_pairs; off += 65535) {
+    const int32_t np = num_pairs - off < 65535 ? num_pairs - off : 65535;
+    const dim3 grid((unsigned)chunks, (unsigned)np, 2);
+    if (wide)
+      hipLaunchKernelGGL(copy_blocks_kernel<uint4>, grid, dim3(kThreads), 0, stream,
+                         (char*)dst_k, (char*)dst_v, (const char*)src_k, (const char*)src_v,
+                         src_ids + off, dst_ids + off, src_blocks, dst_blocks, span_bytes);
+    else
+      hipLaunchKernelGGL(copy_blocks_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                         (char*)dst_k, (char*)dst_v, (const char*)src_k, (const char*)src_v,
+                         src_ids + off, dst_ids + off, src_blocks, dst_blocks, span_bytes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -63,6 +63,13 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            KvType type, hipStream_t stream);
 
+// dst block dst_ids[i] := src block src_ids[i] in both tensors (spans of
+// span_bytes); pairs with an id outside its pool are skipped.
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* src_ids, const int32_t* dst_ids, int32_t num_pairs,
+                              int32_t src_blocks, int32_t dst_blocks, int64_t span_bytes,
+                              hipStream_t stream);
+
 // Returns hipErrorInvalidValue for a (type, D, BS) combination without a kernel.
 // Non-null events are recorded on `stream` right before and right after the
 // attention kernel (not the planner or the merge), for kernel timing.

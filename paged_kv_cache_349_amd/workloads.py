@@ -277,6 +277,35 @@ CONFIG_NAMES = {
 }
 
 
+# Largest context each workload's recipe allows: the reservation a server
+# that sizes every request's KV for its maximum length would make.
+MAX_CONTEXT = {1: 300, 2: 4096, 3: 32768, 4: 2048 + 512 + 1, 5: 8192}
+
+
+def config_lengths(i: int, rng: np.random.Generator, *, long_last: bool = False,
+                   num_seqs: Optional[int] = None) -> np.ndarray:
+    """Context lengths of workload ``i``: the first draws of its recipe."""
+    if i == 1:
+        return np.array([1, 17, 100, 300])
+    if i == 2:
+        lens = rng.integers(128, 4096, size=32, endpoint=True)
+    elif i == 3:
+        lens = np.concatenate([[32768], rng.integers(256, 2048, size=7, endpoint=True)])
+        if long_last:
+            lens = np.concatenate([lens[1:], lens[:1]])
+    elif i == 4:
+        tails = rng.integers(0, 512, size=CFG4_GROUPS * CFG4_SAMPLES, endpoint=True)
+        return CFG4_PROMPT + tails + 1
+    elif i == 5:
+        lens = np.clip(np.rint(rng.lognormal(6.9, 0.6, size=256)), 16, 8192).astype(np.int64)
+    else:
+        raise ValueError(f"no workload {i}")
+    return lens[:num_seqs] if num_seqs else lens
+
+
+CFG4_GROUPS, CFG4_SAMPLES, CFG4_PROMPT = 16, 8, 2048
+
+
 def make_config(i: int, *, seed: Optional[int] = None, poison: str = "nan",
                 block_size: Optional[int] = None, long_last: bool = False,
                 num_seqs: Optional[int] = None) -> Workload:
@@ -287,50 +316,34 @@ def make_config(i: int, *, seed: Optional[int] = None, poison: str = "nan",
     workloads 2, 3 and 5 to their first sequences (same draws) for quick tests.
     """
     rng = np.random.default_rng(SEED_BASE + i if seed is None else seed)
+    lens = config_lengths(i, rng, long_last=long_last, num_seqs=num_seqs)
     if i == 1:
-        lens = np.array([1, 17, 100, 300])
         return build_workload(CONFIG_NAMES[1], rng, kv_dtype=F32, context_lens=lens,
                               num_heads=4, num_kv_heads=4, head_dim=64,
                               block_size=block_size or 16, num_blocks=48, poison=poison,
                               scale=0.125)
     if i == 2:
-        lens = rng.integers(128, 4096, size=32, endpoint=True)
-        if num_seqs:
-            lens = lens[:num_seqs]
         return build_workload(CONFIG_NAMES[2], rng, kv_dtype=BF16, context_lens=lens,
                               num_heads=32, num_kv_heads=8, head_dim=128,
                               block_size=block_size or 16, poison=poison)
     if i == 3:
-        lens = np.concatenate([[32768], rng.integers(256, 2048, size=7, endpoint=True)])
-        if long_last:
-            lens = np.concatenate([lens[1:], lens[:1]])
-        if num_seqs:
-            lens = lens[:num_seqs]
         return build_workload(CONFIG_NAMES[3] + ("-longlast" if long_last else ""), rng,
                               kv_dtype=BF16, context_lens=lens, num_heads=32,
                               num_kv_heads=8, head_dim=128, block_size=block_size or 16,
                               poison=poison)
     if i == 4:
         bs = block_size or 16
-        n_groups, n_samples, prompt = 16, 8, 2048
-        tails = rng.integers(0, 512, size=n_groups * n_samples, endpoint=True)
-        lens = prompt + tails + 1
-        groups = [list(range(g * n_samples, (g + 1) * n_samples)) for g in range(n_groups)]
+        groups = [list(range(g * CFG4_SAMPLES, (g + 1) * CFG4_SAMPLES)) for g in range(CFG4_GROUPS)]
         return build_workload(CONFIG_NAMES[4], rng, kv_dtype=BF16, context_lens=lens,
                               num_heads=32, num_kv_heads=8, head_dim=128, block_size=bs,
-                              shared_prefix_groups=groups, shared_prefix_blocks=prompt // bs,
+                              shared_prefix_groups=groups, shared_prefix_blocks=CFG4_PROMPT // bs,
                               poison=poison)
-    if i == 5:
-        bs = block_size or 16
-        lens = np.clip(np.rint(rng.lognormal(6.9, 0.6, size=256)), 16, 8192).astype(np.int64)
-        if num_seqs:
-            lens = lens[:num_seqs]
-        nblk = int(((lens + bs - 1) // bs).sum())
-        return build_workload(CONFIG_NAMES[5] + f"-bs{bs}", rng, kv_dtype=BF16,
-                              context_lens=lens, num_heads=64, num_kv_heads=8, head_dim=128,
-                              block_size=bs, num_blocks=int(math.ceil(nblk / 0.97)),
-                              poison=poison)
-    raise ValueError(f"no workload {i}")
+    bs = block_size or 16
+    nblk = int(((lens + bs - 1) // bs).sum())
+    return build_workload(CONFIG_NAMES[5] + f"-bs{bs}", rng, kv_dtype=BF16,
+                          context_lens=lens, num_heads=64, num_kv_heads=8, head_dim=128,
+                          block_size=bs, num_blocks=int(math.ceil(nblk / 0.97)),
+                          poison=poison)
 
 
 # --------------------------------------------------------------------------

@@ -149,3 +149,20 @@ def test_kernel_timing_argument_errors(lib):
     assert lib.pa_kernel_timing_begin(-3) == 1
     assert lib.pa_kernel_timing_end(ctypes.byref(ms), ctypes.byref(n)) == 1   # not on
     assert lib.pa_kernel_timing_end(None, ctypes.byref(n)) == 1
+
+
+def test_block_copy_argument_errors(lib):
+    FAKE = 1 << 40
+    args = dict(k=FAKE, v=FAKE, s=FAKE, d=FAKE, n=4, NB=16, Hkv=2, D=8, bs=4, dt=0)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.pa_copy_blocks(a["k"], a["v"], a["s"], a["d"], a["n"], a["NB"], a["Hkv"],
+                                  a["D"], a["bs"], a["dt"], None)
+    assert call(n=-1) == 1
+    assert call(dt=7) == 2
+    assert call(NB=0) == 1
+    assert call(s=None) == 1
+    assert call(n=0, k=None, v=None, s=None, d=None) == 0
+    assert lib.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, 5, 2, 8, 4, 1, None) == 1
+    assert lib.pa_swap_blocks(None, None, None, None, None, None, 0, 5, 5, 2, 8, 4, 1, None) == 0
