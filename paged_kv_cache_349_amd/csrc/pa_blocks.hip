@@ -18,6 +18,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;   // 16-byte vectors in flight per thread
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Source spans are read once: nontemporal loads stream them past the caches
+// (measured on 4096 pairs of 32 KB spans: 4.9 TB/s against 3.9 TB/s with
+// ordinary loads; nontemporal stores did not help and are not used).
+__device__ inline uint4 stream_load(const uint4* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ inline uint16_t stream_load(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 template <typename V>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     char* __restrict__ dst_k, char* __restrict__ dst_v, const char* __restrict__ src_k,
@@ -39,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t i = base + (int64_t)u * kThreads;
-    if (i < n) buf[u] = f[i];
+    if (i < n) buf[u] = stream_load(f + i);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
