@@ -185,6 +185,49 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
                                     int32_t block_size, int32_t kv_dtype,
                                     int32_t partition_tokens);
 
+/*
+ * Decode attention with shared prompt prefixes.  Same result as pa_decode
+ * (up to the rounding of a different reduction order), for a batch in which
+ * groups of consecutive sequences -- e.g. parallel samples or beams forked
+ * from one prompt -- hold the same leading physical blocks ("How does vLLM
+ * PagedAttention manage Virtual Memory Pages ...", section "Key Technical
+ * Innovations", item 3: copy-on-write sharing of prompt blocks; "PagedAttention
+ * and KV memory management", section "Myths and failure modes": without
+ * sharing, n samples multiply the prompt's KV by n).  Each shared K/V tile is
+ * read once for all the group's sequences and query heads (up to 32 query
+ * rows per read, with matrix-core products), instead of once per sequence.
+ *
+ *   group_starts   [num_groups + 1] int32, device: group g is sequences
+ *                  group_starts[g] .. group_starts[g+1]-1 (non-decreasing;
+ *                  sequences outside every group are decoded as usual)
+ *   prefix_blocks  [num_groups] int32, device: leading table entries that
+ *                  every sequence of group g has in common.  Only whole
+ *                  blocks inside every member's context are treated as
+ *                  shared: the kernel uses min(prefix_blocks[g],
+ *                  min over members of context_len / block_size).  They are
+ *                  read through the group's first table; tables that differ
+ *                  there give an unspecified result (never an out-of-bounds
+ *                  access).
+ *   num_groups == 0 gives plain pa_decode results.
+ * Supported: kv_dtype BF16, the shapes of pa_decode, num_seqs <= 8192.  Other
+ * dtypes return PA_ERR_UNSUPPORTED.  The workspace must hold
+ * pa_decode_shared_prefix_workspace_bytes(...) bytes (partition_tokens as in
+ * pa_decode_ex; 0 = the library's choice).
+ */
+int pa_decode_shared_prefix(float* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* group_starts, const int32_t* prefix_blocks,
+                            int32_t num_groups, float scale, int32_t block_size, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+                            void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                            void* stream);
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t kv_dtype, int32_t partition_tokens);
+
 /* Tokens per partition that pa_decode picks for these shapes (0 if invalid). */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_blocks_per_seq, int32_t block_size);

@@ -46,6 +46,9 @@ _SIGNATURES = {
                   [_vp, ctypes.c_size_t, _vp]),
     "pa_decode_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float] + [_c_int] * 8 +
                      [_vp, ctypes.c_size_t, _c_int, _c_int, _vp]),
+    "pa_decode_shared_prefix": (ctypes.c_int, [_vp] * 8 + [_c_int, ctypes.c_float] + [_c_int] * 8 +
+                                [_vp, ctypes.c_size_t, _c_int, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [_c_int] * 8),
     "pa_kernel_timing_begin": (ctypes.c_int, [_c_int]),
     "pa_kernel_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(_c_int)]),
@@ -245,6 +248,45 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     return out
 
 
+def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                         prefix_blocks, scale, block_size, stream=None, *, workspace=None,
+                         partition_tokens=0):
+    """decode() for a batch whose groups of consecutive sequences share leading blocks.
+
+    group_starts: int32 [num_groups + 1] (device), prefix_blocks: int32 [num_groups].
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
+                  prefix_blocks)
+    NB, Hkv, bs, D = _pool_shape(k_cache, v_cache)
+    _need(bs == block_size, f"block_size={block_size} but k_cache has {bs}")
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
+    S, Hq, _ = q.shape
+    _need(q.dtype == k_cache.dtype, "q and caches must share a dtype")
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, D), "out: float32 [S, Hq, D]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens: int32 [S]")
+    ng = prefix_blocks.shape[0] if prefix_blocks.dim() == 1 else -1
+    _need(group_starts.dtype == torch.int32 and prefix_blocks.dtype == torch.int32 and ng >= 0 and
+          tuple(group_starts.shape) == (ng + 1,), "group_starts int32 [G + 1], prefix_blocks int32 [G]")
+    code = _dtype_code(k_cache)
+    max_blocks = block_tables.shape[1]
+    need = int(lib.pa_decode_shared_prefix_workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code,
+                                                           partition_tokens))
+    sh = _stream_handle(dev, stream)
+    if workspace is None:
+        workspace = _workspace(dev, sh, need)
+    _check(lib.pa_decode_shared_prefix(
+        out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), group_starts.data_ptr(),
+        prefix_blocks.data_ptr(), ng, float(scale), bs, S, Hq, Hkv, D, max_blocks, NB, code,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), partition_tokens, sh))
+    return out
+
+
 def kernel_timing_begin(capacity: int):
     """Time the attention kernel of the next `capacity` decode calls (see the C header)."""
     _check(load_library().pa_kernel_timing_begin(int(capacity)))
@@ -258,5 +300,5 @@ def kernel_timing_end():
     return ms.value, n.value
 
 
-__all__ = ["write_kv", "decode", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+__all__ = ["write_kv", "decode", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
            "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]

@@ -50,6 +50,8 @@ constexpr double kLog2e = 1.4426950408889634;
 // the ratio).  The workspace is sized for the smallest.
 constexpr int32_t kMinPartitionTokens = 256;
 constexpr int32_t kMaxPartitionTokens = 8192;
+// The planner keeps per-sequence lengths and prefix starts in LDS.
+constexpr int32_t kMaxPrefixSeqs = 8192;
 
 int32_t min_partition_tokens(int32_t block_size) {
   const int32_t t = kMinPartitionTokens < block_size ? block_size : kMinPartitionTokens;
@@ -58,21 +60,25 @@ int32_t min_partition_tokens(int32_t block_size) {
 
 // Workspace regions, each 256-byte aligned: planner outputs, work list, list
 // of split sequences, and (when a sequence may span several partitions) the
-// partition states.
+// partition states.  With shared prefixes: one more partition per sequence
+// (the prefix is cut on its own, so the cuts may add one partition), the
+// prefix work list, and partition states always (every sequence with a
+// shared prefix is merged).
 struct Layout {
   int32_t part_blocks = 0;
   int32_t num_parts_max = 0;
-  size_t ctrl_off = 0, items_off = 0, split_off = 0, acc_off = 0, ml_off = 0;
+  size_t ctrl_off = 0, items_off = 0, split_off = 0, acc_off = 0, ml_off = 0, pitems_off = 0;
   size_t total = 0;
 };
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                        int32_t max_blocks, int32_t block_size, int32_t partition_tokens) {
+                        int32_t max_blocks, int32_t block_size, int32_t partition_tokens,
+                        bool prefix = false) {
   Layout l;
   l.part_blocks = partition_tokens / block_size;
-  l.num_parts_max = (max_blocks + l.part_blocks - 1) / l.part_blocks;
+  l.num_parts_max = (max_blocks + l.part_blocks - 1) / l.part_blocks + (prefix ? 1 : 0);
   size_t off = 0;
   l.ctrl_off = off;
   off += align256(pa::kCtrlSize * sizeof(int32_t));
@@ -86,6 +92,10 @@ Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
     off += align256(rows * head_dim * sizeof(float));
     l.ml_off = off;
     off += align256(rows * 2 * sizeof(float));
+  }
+  if (prefix) {
+    l.pitems_off = off;
+    off += align256((size_t)num_seqs * l.num_parts_max * 4 * sizeof(int32_t));
   }
   l.total = off;
   return l;
@@ -126,6 +136,105 @@ bool shapes_valid(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int
                   int32_t max_blocks, int32_t block_size) {
   return num_seqs >= 0 && num_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_blocks > 0 &&
          block_size > 0 && num_heads % num_kv_heads == 0;
+}
+
+static int decode_common(float* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, int32_t kv_dtype, void* workspace,
+                         size_t workspace_bytes, int32_t partition_tokens, int32_t flags,
+                         const int32_t* group_starts, const int32_t* prefix_blocks,
+                         int32_t num_groups, bool prefix, void* stream) {
+  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
+  if (num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "sizes must be positive (num_heads=%d num_kv_heads=%d head_dim=%d block_size=%d "
+                "max_blocks_per_seq=%d num_blocks=%d)",
+                num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads=%d is not a multiple of num_kv_heads=%d",
+                num_heads, num_kv_heads);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (flags & ~PA_FLAG_VECTOR_ALU) return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  const int32_t group = num_heads / num_kv_heads;
+  if (!pa::decode_supported((pa::KvType)kv_dtype, head_dim, block_size, group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "no kernel for head_dim=%d block_size=%d group=%d (compiled: head_dim 64/128, "
+                "block_size 16/32, group 1..16)",
+                head_dim, block_size, group);
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
+      (int64_t)num_seqs * num_heads * head_dim > INT32_MAX * 4LL)
+    return fail(PA_ERR_UNSUPPORTED, "shape too large");
+  const bool adaptive = partition_tokens == 0;
+  if (adaptive) partition_tokens = min_partition_tokens(block_size);
+  if (partition_tokens < block_size || partition_tokens % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_tokens=%d is not a positive multiple of %d",
+                partition_tokens, block_size);
+  if (prefix) {
+    if (num_groups < 0) return fail(PA_ERR_INVALID_ARG, "num_groups=%d < 0", num_groups);
+    if (kv_dtype != PA_DTYPE_BF16 || (flags & PA_FLAG_VECTOR_ALU))
+      return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode runs the bf16 matrix-core kernels only");
+    if (num_seqs > kMaxPrefixSeqs)
+      return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode handles at most %d sequences",
+                  kMaxPrefixSeqs);
+  }
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null device pointer");
+  if (prefix && num_groups > 0 && (!group_starts || !prefix_blocks))
+    return fail(PA_ERR_INVALID_ARG, "null group array with num_groups=%d", num_groups);
+  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
+  const Layout lay = workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                      block_size, partition_tokens, prefix);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
+                workspace_bytes, workspace, lay.total);
+  if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > (INT32_MAX >> 1) ||
+      (int64_t)max_blocks_per_seq * num_seqs > (INT32_MAX >> 1))
+    return fail(PA_ERR_UNSUPPORTED, "too many work items");
+
+  pa::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.scale_log2 = (float)((double)scale * kLog2e);
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.part_blocks_min = lay.part_blocks;
+  const int32_t max_tokens = kMaxPartitionTokens < block_size ? block_size : kMaxPartitionTokens;
+  p.part_blocks_max = adaptive ? max_tokens / block_size : lay.part_blocks;
+  p.num_parts_max = lay.num_parts_max;
+  p.balance = adaptive ? 1 : 0;   // the launcher sets the ratio
+  p.decode_grid = 0;
+  char* ws = (char*)workspace;
+  p.ws_ctrl = (int32_t*)(ws + lay.ctrl_off);
+  p.ws_items = (int4*)(ws + lay.items_off);
+  p.ws_split = (int2*)(ws + lay.split_off);
+  p.ws_acc = lay.num_parts_max > 1 ? (float*)(ws + lay.acc_off) : nullptr;
+  p.ws_ml = lay.num_parts_max > 1 ? (float*)(ws + lay.ml_off) : nullptr;
+  p.group_starts = prefix ? group_starts : nullptr;
+  p.prefix_blocks = prefix ? prefix_blocks : nullptr;
+  p.num_groups = prefix ? num_groups : 0;
+  p.prefix_rows = 0;   // set by the launcher
+  p.ws_pitems = prefix ? (int4*)(ws + lay.pitems_off) : nullptr;
+  const auto ev = next_timing_events();
+  hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
+                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream,
+                                   ev.first, ev.second);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // namespace
@@ -243,80 +352,38 @@ int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_c
                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks,
                  int32_t kv_dtype, void* workspace, size_t workspace_bytes,
                  int32_t partition_tokens, int32_t flags, void* stream) {
-  if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
-  if (num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return fail(PA_ERR_INVALID_ARG,
-                "sizes must be positive (num_heads=%d num_kv_heads=%d head_dim=%d block_size=%d "
-                "max_blocks_per_seq=%d num_blocks=%d)",
-                num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks);
-  if (num_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "num_heads=%d is not a multiple of num_kv_heads=%d",
-                num_heads, num_kv_heads);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (flags & ~PA_FLAG_VECTOR_ALU) return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  const int32_t group = num_heads / num_kv_heads;
-  if (!pa::decode_supported((pa::KvType)kv_dtype, head_dim, block_size, group))
-    return fail(PA_ERR_UNSUPPORTED,
-                "no kernel for head_dim=%d block_size=%d group=%d (compiled: head_dim 64/128, "
-                "block_size 16/32, group 1..16)",
-                head_dim, block_size, group);
-  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX ||
-      (int64_t)num_seqs * num_heads * head_dim > INT32_MAX * 4LL)
-    return fail(PA_ERR_UNSUPPORTED, "shape too large");
-  const bool adaptive = partition_tokens == 0;
-  if (adaptive) partition_tokens = min_partition_tokens(block_size);
-  if (partition_tokens < block_size || partition_tokens % block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_tokens=%d is not a positive multiple of %d",
-                partition_tokens, block_size);
-  if (num_seqs == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID_ARG, "null device pointer");
-  if (((uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
-    return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
-  const Layout lay = workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq,
-                                      block_size, partition_tokens);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
-                workspace_bytes, workspace, lay.total);
-  if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > (INT32_MAX >> 1) ||
-      (int64_t)max_blocks_per_seq * num_seqs > (INT32_MAX >> 1))
-    return fail(PA_ERR_UNSUPPORTED, "too many work items");
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, kv_dtype, workspace, workspace_bytes, partition_tokens, flags,
+                       nullptr, nullptr, 0, false, stream);
+}
 
-  pa::DecodeParams p;
-  p.out = out;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.tables = block_tables;
-  p.lens = context_lens;
-  p.scale_log2 = (float)((double)scale * kLog2e);
-  p.num_seqs = num_seqs;
-  p.num_heads = num_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.group = group;
-  p.max_blocks = max_blocks_per_seq;
-  p.num_blocks = num_blocks;
-  p.part_blocks_min = lay.part_blocks;
-  const int32_t max_tokens = kMaxPartitionTokens < block_size ? block_size : kMaxPartitionTokens;
-  p.part_blocks_max = adaptive ? max_tokens / block_size : lay.part_blocks;
-  p.num_parts_max = lay.num_parts_max;
-  p.balance = adaptive ? 1 : 0;   // the launcher sets the ratio
-  p.decode_grid = 0;
-  char* ws = (char*)workspace;
-  p.ws_ctrl = (int32_t*)(ws + lay.ctrl_off);
-  p.ws_items = (int4*)(ws + lay.items_off);
-  p.ws_split = (int2*)(ws + lay.split_off);
-  p.ws_acc = lay.num_parts_max > 1 ? (float*)(ws + lay.acc_off) : nullptr;
-  p.ws_ml = lay.num_parts_max > 1 ? (float*)(ws + lay.ml_off) : nullptr;
-  const auto ev = next_timing_events();
-  hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
-                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream,
-                                   ev.first, ev.second);
-  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
-  return ok();
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_blocks_per_seq, int32_t block_size,
+                                               int32_t kv_dtype, int32_t partition_tokens) {
+  (void)kv_dtype;
+  if (!shapes_valid(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size))
+    return 0;
+  if (partition_tokens == 0) partition_tokens = min_partition_tokens(block_size);
+  if (partition_tokens < block_size || partition_tokens % block_size != 0) return 0;
+  return workspace_layout(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size,
+                          partition_tokens, true)
+      .total;
+}
+
+int pa_decode_shared_prefix(float* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* group_starts, const int32_t* prefix_blocks,
+                            int32_t num_groups, float scale, int32_t block_size, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+                            void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                            void* stream) {
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, kv_dtype, workspace, workspace_bytes, partition_tokens, 0,
+                       group_starts, prefix_blocks, num_groups, true, stream);
 }
 
 int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,

@@ -117,48 +117,86 @@ constexpr int kLensCached = 8192;   // context lengths the planner keeps in LDS
 
 __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
   __shared__ int lens_c[kLensCached];
+  __shared__ int start_c[kLensCached];   // shared-prefix blocks per sequence
   __shared__ int cls_off[kTailClasses];
   __shared__ int wave_sum[16];
   __shared__ int run_base;
   __shared__ int nsplit;
+  __shared__ int npitems;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.num_seqs;
+  const bool prefix = a.num_groups > 0;   // then S <= kLensCached (checked on the host)
 
   for (int i = tid; i < kTailClasses; i += 1024) cls_off[i] = 0;
   if (tid == 0) {
     run_base = 0;
     nsplit = 0;
+    npitems = 0;
   }
   // One pass over the context lengths (clamped), kept in LDS for the passes
-  // below, and the total block count.  S * max_blocks fits in int32 (checked
-  // on the host).
-  int mine = 0;
+  // below.  S * max_blocks fits in int32 (checked on the host).
   for (int s = tid; s < S; s += 1024) {
-    const int L = clamp_len(a, s, block_size);
-    if (s < kLensCached) lens_c[s] = L;
-    mine += (L + block_size - 1) / block_size;
+    if (s < kLensCached) lens_c[s] = clamp_len(a, s, block_size);
+    if (prefix) start_c[s] = 0;
   }
-  const int64_t total = block_sum_1024(mine, wave_sum);   // also publishes lens_c
+  __syncthreads();
   auto len_of = [&](int s) { return s < kLensCached ? lens_c[s] : clamp_len(a, s, block_size); };
+  auto start_of = [&](int s) { return prefix ? start_c[s] : 0; };
+
+  // Shared prefixes.  A group's prefix is the run of whole blocks that its
+  // table entries share and that lies inside every member's context; it is
+  // read once per `per_item` sequences.  A group of one shares nothing.
+  const int per_item = prefix ? (a.prefix_rows / a.group > 0 ? a.prefix_rows / a.group : 1) : 1;
+  auto group_range = [&](int g, int& lo, int& hi) {
+    lo = max(a.group_starts[g], 0);
+    hi = min(a.group_starts[g + 1], S);
+  };
+  int pre_mine = 0;
+  if (prefix) {
+    for (int g = tid; g < a.num_groups; g += 1024) {
+      int lo, hi;
+      group_range(g, lo, hi);
+      if (hi - lo < 2) continue;
+      int minL = len_of(lo);
+      for (int s = lo + 1; s < hi; ++s) minL = min(minL, len_of(s));
+      const int P = min(a.prefix_blocks[g], minL / block_size);
+      if (P <= 0) continue;
+      for (int s = lo; s < hi; ++s) start_c[s] = P;
+      pre_mine += (hi - lo + per_item - 1) / per_item * P;
+    }
+  }
+  const int64_t pre_total = block_sum_1024(pre_mine, wave_sum);   // also publishes start_c
+  int mine = 0;
+  for (int s = tid; s < S; s += 1024)
+    mine += (len_of(s) + block_size - 1) / block_size - start_of(s);
+  const int64_t total = block_sum_1024(mine, wave_sum);
 
   // Partition size: the largest pb = part_blocks_min * 2^k (<= part_blocks_max)
   // whose partitions are each at most 1/balance of one workgroup's share of
   // all blocks.  Long partitions mean few partition states to merge; short
-  // ones spread a long context over many workgroups.
-  int pb = a.part_blocks_min;
-  if (a.balance > 0) {
-    const int64_t share = total * a.num_kv_heads / ((int64_t)a.decode_grid * a.balance);
-    for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share &&
-                    pb * 2 <= a.part_blocks_max; ++k)
-      pb *= 2;
-  }
+  // ones spread a long context over many workgroups.  Prefix partitions are
+  // sized the same way from the prefix work alone (uniform items, no balance
+  // margin).
+  auto pick = [&](int64_t work, int balance) {
+    int pb = a.part_blocks_min;
+    if (balance > 0) {
+      const int64_t share = work * a.num_kv_heads / ((int64_t)a.decode_grid * balance);
+      for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share &&
+                      pb * 2 <= a.part_blocks_max; ++k)
+        pb *= 2;
+    }
+    return pb;
+  };
+  const int pb = pick(total, a.balance);
+  const int pbp = pick(pre_total, a.balance > 0 ? 1 : 0);
   if (tid == 0) {
     a.ws_ctrl[kCtrlPartBlocks] = pb;
+    a.ws_ctrl[kCtrlPrefixPart] = pbp;
     a.ws_ctrl[kCtrlAbort] = 0;
   }
 
-  // Partial last partition of a sequence: size class, larger partitions in
-  // lower classes.  -1 if the sequence has no partial partition.
+  // Partial last partition of a sequence's own blocks: size class, larger
+  // partitions in lower classes.  -1 if there is no partial partition.
   auto tail_class = [&](int nblk) {
     const int rem = nblk % pb;
     if (rem == 0) return -1;
@@ -167,17 +205,22 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
 
   // Pass 1: full partitions in sequence order (an empty sequence gets one
   // item that zeroes its output); count partial partitions per class; list
-  // the sequences that span several partitions.
+  // the sequences whose states are merged: those spanning several partitions
+  // and all that have a shared prefix (prefix partitions come first).
   for (int c0 = 0; c0 < S; c0 += 1024) {
     const int s = c0 + tid;
-    int nfull = 0, L = 0;
+    int nfull = 0, L = 0, P = 0;
     if (s < S) {
       L = len_of(s);
-      const int nblk = (L + block_size - 1) / block_size;
-      nfull = nblk == 0 ? 1 : nblk / pb;
+      P = start_of(s);
+      const int nblk = (L + block_size - 1) / block_size - P;
+      nfull = nblk == 0 ? (P == 0 ? 1 : 0) : nblk / pb;
       const int c = tail_class(nblk);
       if (c >= 0) atomicAdd(&cls_off[c], 1);
-      if (nblk > pb) a.ws_split[atomicAdd(&nsplit, 1)] = make_int2(s, (nblk + pb - 1) / pb);
+      const int nown = (nblk + pb - 1) / pb;
+      const int npre = (P + pbp - 1) / pbp;
+      if (npre + nown > 1 || npre > 0)
+        a.ws_split[atomicAdd(&nsplit, 1)] = make_int2(s, npre + nown);
     }
     int incl = nfull;
 #pragma unroll
@@ -193,7 +236,7 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
       chunk += wave_sum[w];
     }
     const int base = run_base + before + incl - nfull;
-    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, 0);
+    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, P);
     __syncthreads();
     if (tid == 0) run_base += chunk;
     __syncthreads();
@@ -227,9 +270,31 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
   // changes which workgroup computes an item, never the result.
   for (int s = tid; s < S; s += 1024) {
     const int L = len_of(s);
-    const int nblk = (L + block_size - 1) / block_size;
+    const int P = start_of(s);
+    const int nblk = (L + block_size - 1) / block_size - P;
     const int c = tail_class(nblk);
-    if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int4(s, nblk / pb, L, 0);
+    if (c >= 0) a.ws_items[atomicAdd(&cls_off[c], 1)] = make_int4(s, nblk / pb, L, P);
+  }
+
+  // Prefix work list: (first sequence, sequences, partition, prefix blocks)
+  // for every run of per_item sequences of a group and every partition of
+  // its prefix.  The order is arbitrary (it never changes the result).
+  if (prefix) {
+    for (int g = tid; g < a.num_groups; g += 1024) {
+      int lo, hi;
+      group_range(g, lo, hi);
+      if (hi - lo < 2) continue;
+      const int P = start_c[lo];
+      if (P <= 0) continue;
+      const int np = (P + pbp - 1) / pbp;
+      for (int f = lo; f < hi; f += per_item) {
+        const int n = min(per_item, hi - f);
+        const int at = atomicAdd(&npitems, np);
+        for (int p = 0; p < np; ++p) a.ws_pitems[at + p] = make_int4(f, n, p, P);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) a.ws_ctrl[kCtrlPrefixItems] = npitems;
   }
 }
 
@@ -457,6 +522,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   const PA_CONST int32_t* tables = as_const(a.tables);
   const int total = ctrl[kCtrlEntries] * Hkv;
   const int pb = ctrl[kCtrlPartBlocks];
+  const int pbp = ctrl[kCtrlPrefixPart];
   __shared__ int s_count[kMaxLdsSlots];   // waves that finished the slot's item
   __shared__ int s_epoch[kMaxLdsSlots];   // item the slot is free for
 
@@ -486,10 +552,15 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     d.part = items[4 * e_idx + 1];
     d.L = d.valid ? items[4 * e_idx + 2] : 0;
     d.h = d.valid ? item - e_idx * Hkv : 0;
+    // Blocks before P belong to the sequence's shared prefix, computed by
+    // the prefix kernel as the first partition states of the sequence.
+    const int P = d.valid ? items[4 * e_idx + 3] : 0;
     const int nblk = (d.L + BS - 1) / BS;
-    d.b0 = d.part * pb;
+    d.b0 = P + d.part * pb;
     const int nb = min(d.b0 + pb, nblk) - d.b0;
-    d.nparts = (nblk + pb - 1) / pb;
+    const int npre = (P + pbp - 1) / pbp;
+    d.nparts = npre + (nblk - P + pb - 1) / pb;
+    d.part += npre;
     // Rotating the waves' lanes from item to item spreads the extra blocks of
     // items whose size is not a multiple of W evenly over the waves.
     d.wr = (w + r) & (W - 1);
@@ -751,6 +822,213 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 }
 
 // ---------------------------------------------------------------------------
+// Shared-prefix kernel, bf16 KV.
+// ---------------------------------------------------------------------------
+
+// Query rows of one prefix item: two 16-column halves of the MFMA tiles.
+constexpr int kPrefixRows = 32;
+
+// LDS of the prefix kernel: per wave, (max, sum) and weighted sums of the 32 rows.
+template <int D, int W>
+__host__ __device__ constexpr int prefix_lds_floats() {
+  return 2 * W * kPrefixRows + W * kPrefixRows * (D + 4);
+}
+
+// Parallel samples of one prompt ("How does vLLM PagedAttention manage
+// Virtual Memory Pages ...", section "Key Technical Innovations", item 3)
+// hold the prompt's blocks once; this kernel reads each of those K/V tiles
+// once for all the sequences of a prefix item and all their query heads:
+// up to 32 query rows (sequence-major, head-minor) in two 16-column halves,
+//   S^T[16 tokens x 16 rows] = K[16 x D] * Q^T[D x 16]        per half
+//   O^T[16 d x 16 rows]     += V^T[16 d x 16] * P^T[16 x 16]  per half
+// so one tile feeds 32 rows' scores and weighted sums.  Work item =
+// (prefix item, KV head); the W waves take the item's blocks b0 + w,
+// b0 + w + W, ... with two tile buffers in flight, and their states are
+// merged through LDS in wave order.  The result of each sequence's rows is
+// stored as its partition state number `part` (prefix partitions precede
+// the sequence's own partitions), for merge_splits.  Prefix blocks are whole
+// and inside every member's context, so nothing is masked except blocks
+// whose id is outside the pool (which then contribute nothing).
+template <int D, int BS, int W>
+__global__ __launch_bounds__(64 * W) void prefix_mfma_bf16(DecodeParams a) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, quad = lane >> 4;
+  const int G = a.group, Hkv = a.num_kv_heads, Hq = a.num_heads;
+  const PA_CONST int32_t* ctrl = as_const(a.ws_ctrl);
+  const PA_CONST int32_t* pitems = as_const((const int32_t*)a.ws_pitems);
+  const PA_CONST int32_t* tables = as_const(a.tables);
+  const int total = ctrl[kCtrlPrefixItems] * Hkv;
+  const int pbp = ctrl[kCtrlPrefixPart];
+  float* sm_m = smem;
+  float* sm_l = smem + W * kPrefixRows;
+  float* sm_acc = smem + 2 * W * kPrefixRows;
+  const uint32_t tile_bytes = (uint32_t)BS * D * 2;
+  const LaneOff lo = lane_offsets<D, BS>(lane, G);
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int e = item / Hkv;
+    const int kv = item - e * Hkv;
+    const int first = pitems[4 * e + 0], nseq = pitems[4 * e + 1];
+    const int part = pitems[4 * e + 2], P = pitems[4 * e + 3];
+    const int b0 = part * pbp, b1 = min(b0 + pbp, P);
+    const int rows = nseq * G;
+
+    // Query operands: row r = 16 * half + col is head r % G of sequence
+    // first + r / G; rows past the item's sequences read zeros.
+    bf16x8 qop[2][D / 32];
+    {
+      const uint32_t qbytes = (uint32_t)nseq * Hq * D * 2;
+      const __amdgpu_buffer_rsrc_t qr =
+          buffer_of((const char*)a.q + (int64_t)first * Hq * D * 2, qbytes);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = hh * 16 + col;
+        const uint32_t off = r < rows ? ((uint32_t)((r / G) * Hq + kv * G + r % G) * D + quad * 8) * 2
+                                      : qbytes;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          qop[hh][c] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off + c * 64, 0, 0));
+      }
+    }
+
+    float m[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
+    f32x4 acc[2][D / 16];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t trow = (int64_t)first * a.max_blocks;
+    // Loads of block j (of the first member's table) into t; positions past
+    // the item's blocks or with an id outside the pool read zeros.
+    auto load_blk = [&](Tile<D, BS>& t, int j, bool& has) {
+      int id = 0;
+      if (j < b1) id = tables[trow + j];
+      has = j < b1 && (unsigned)id < (unsigned)a.num_blocks;
+      const int64_t off = has ? ((int64_t)id * Hkv + kv) * tile_bytes : 0;
+      const uint32_t nb = has ? tile_bytes : 0;
+      load_tile<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo);
+    };
+
+    auto compute = [&](Tile<D, BS>& t, bool has) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x4 sc[Tile<D, BS>::SB];
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb) {
+          sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+            sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sb][c], qop[hh][c], sc[sb], 0, 0, 0);
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float x = has ? sc[sb][rr] * a.scale_log2 : kNegInf;
+            sc[sb][rr] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mnew = fmaxf(m[hh], mx);
+        const float mref = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = exp2_fast(m[hh] - mref);
+        m[hh] = mnew;
+        i16x4 pw[Tile<D, BS>::SB];
+        float psum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
+            pw[sb][rr] = (short)bits;
+            psum += bf16_bits_to_f32(bits);
+          }
+        lsum[hh] = lsum[hh] * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+          for (int i = 0; i < D / 16; ++i) acc[hh][i] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+          for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+            acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[hh][i],
+                                                                   0, 0, 0);
+      }
+    };
+
+    // Two buffers in flight: every step issues the loads of the position
+    // two ahead, then computes the oldest one.
+    Tile<D, BS> t0, t1;
+    bool h0 = false, h1 = false;
+    int j = b0 + w;
+    load_blk(t0, j, h0);
+    for (;;) {
+      load_blk(t1, j + W, h1);
+      if (j >= b1) break;
+      compute(t0, h0);
+      j += W;
+      load_blk(t0, j + W, h0);
+      if (j >= b1) break;
+      compute(t1, h1);
+      j += W;
+    }
+
+    // Wave state -> LDS (row r of half hh is column col).
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float ls = lsum[hh];
+      ls += shfl_xor_f(ls, 16);
+      ls += shfl_xor_f(ls, 32);
+      const int r = hh * 16 + col;
+      if (quad == 0) {
+        sm_m[w * kPrefixRows + r] = m[hh];
+        sm_l[w * kPrefixRows + r] = ls;
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+        *reinterpret_cast<f32x4*>(&sm_acc[(w * kPrefixRows + r) * (D + 4) + i * 16 + quad * 4]) =
+            acc[hh][i];
+    }
+    __syncthreads();
+    // Merge the W wave states in wave order and store each member's rows as
+    // its partition state `part`.
+    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += 64 * W) {
+      const int r = idx / (D / 4);
+      const int d4 = idx - r * (D / 4);
+      float M = kNegInf;
+#pragma unroll
+      for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v * kPrefixRows + r]);
+      float lam = 0.f;
+      f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float mv = sm_m[v * kPrefixRows + r];
+        const float c = mv == kNegInf ? 0.f : exp2_fast(mv - M);
+        lam += sm_l[v * kPrefixRows + r] * c;
+        val += *reinterpret_cast<const f32x4*>(&sm_acc[(v * kPrefixRows + r) * (D + 4) + d4 * 4]) * c;
+      }
+      const int sq = first + r / G, g = r % G;
+      const int64_t row = (((int64_t)sq * Hkv + kv) * a.num_parts_max + part) * G + g;
+      *reinterpret_cast<f32x4*>(a.ws_acc + row * D + d4 * 4) = val;
+      if (d4 == 0) {
+        a.ws_ml[row * 2 + 0] = M;
+        a.ws_ml[row * 2 + 1] = lam;
+      }
+    }
+    __syncthreads();   // LDS is reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel (fp32 KV; also bf16 when asked).
 // ---------------------------------------------------------------------------
 
@@ -988,9 +1266,21 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   const int64_t max_items = (int64_t)p.num_seqs * p.num_parts_max * p.num_kv_heads;
   p.decode_grid = (int)(max_items < resident ? max_items : resident);
 
+  p.prefix_rows = kPrefixRows;
   hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.num_groups > 0) {
+    // Shared prefixes (bf16, matrix cores only; checked by the API).
+    const void* pk = (const void*)prefix_mfma_bf16<D, BS, kWaves>;
+    const size_t psmem = (size_t)prefix_lds_floats<D, kWaves>() * 4;
+    const int pres = resident_workgroups(pk, threads, psmem);
+    if (pres <= 0) return hipErrorInvalidDeviceFunction;
+    const int pgrid = (int)(max_items < pres ? max_items : pres);
+    hipLaunchKernelGGL((prefix_mfma_bf16<D, BS, kWaves>), dim3(pgrid), dim3(threads), psmem,
+                       stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
   if (type == KvType::BF16 && !vector_alu)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),

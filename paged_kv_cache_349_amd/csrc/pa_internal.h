@@ -35,9 +35,18 @@ struct DecodeParams {
   int32_t lds_records;        // LDS output records of the matrix-core kernel (set by the launcher)
   float* ws_acc;              // [S, Hkv, num_parts_max, group, D] partition sums
   float* ws_ml;               // [S, Hkv, num_parts_max, group, 2] partition (max, sum)
-  int4* ws_items;             // [S * num_parts_max] work list: (sequence, partition, length, 0)
+  int4* ws_items;             // [S * num_parts_max] work list: (sequence, partition, length,
+                              //  first block: the sequence's shared-prefix blocks, else 0)
   int2* ws_split;             // [S] (sequence, partitions) of sequences spanning several
   int32_t* ws_ctrl;           // [kCtrlSize] written by the planner
+  // Shared prefixes (num_groups == 0: none).  Sequences group_starts[g] ..
+  // group_starts[g+1]-1 share their first prefix_blocks[g] table entries.
+  const int32_t* group_starts;  // [num_groups + 1]
+  const int32_t* prefix_blocks; // [num_groups]
+  int32_t num_groups;
+  int32_t prefix_rows;          // query rows one prefix item serves (its sequences x group)
+  int4* ws_pitems;              // [S * num_parts_max] prefix work list:
+                                //  (first sequence, sequences, partition, prefix blocks)
 };
 
 // ws_ctrl slots written by the planner: work-list entries, chosen partition
@@ -45,6 +54,8 @@ struct DecodeParams {
 constexpr int kCtrlEntries = 0;
 constexpr int kCtrlPartBlocks = 1;
 constexpr int kCtrlSplits = 2;
+constexpr int kCtrlPrefixItems = 3;   // entries of the prefix work list
+constexpr int kCtrlPrefixPart = 4;    // blocks per prefix partition
 // Set by the decode kernel if one of its waits on other waves of its
 // workgroup did not end (a broken invariant; the output is then incomplete).
 // Tests read it; cleared by the planner.

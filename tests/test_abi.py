@@ -166,3 +166,20 @@ def test_block_copy_argument_errors(lib):
     assert call(n=0, k=None, v=None, s=None, d=None) == 0
     assert lib.pa_swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, 5, 2, 8, 4, 1, None) == 1
     assert lib.pa_swap_blocks(None, None, None, None, None, None, 0, 5, 5, 2, 8, 4, 1, None) == 0
+
+
+def test_shared_prefix_workspace_and_errors(lib):
+    parts = 11 + 1                # ceil(161 / 16) partitions, + 1 for the prefix cut
+    rows = 128 * 32 * parts       # S * Hq * partitions
+    n = lib.pa_decode_shared_prefix_workspace_bytes(128, 32, 8, 128, 161, 16, 1, 256)
+    assert n == 256 + _align(128 * parts * 16) + _align(128 * 8) + _align(rows * 128 * 4) + \
+        _align(rows * 8) + _align(128 * parts * 16)
+    assert lib.pa_decode_shared_prefix_workspace_bytes(4, 6, 4, 64, 4, 16, 1, 0) == 0
+    FAKE = 1 << 40
+    call = lambda dt, ng, S=4: lib.pa_decode_shared_prefix(
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ng, 0.5, 16, S, 8, 2, 128, 4, 64, dt,
+        FAKE, 1 << 30, 0, None)
+    assert call(0, 1) == 2            # fp32: not supported
+    assert call(1, -1) == 1
+    assert call(1, 1, S=9000) == 2    # more sequences than the planner keeps
+    assert call(1, 1, S=0) == 0       # empty batch
