@@ -142,10 +142,41 @@ class Workload:
         tab = int(self.blocks_per_seq().sum()) * 4 + self.num_seqs * 4
         return q + out + tab
 
+    def prefix_groups(self):
+        """(group_starts [G+1], prefix_blocks [G]) of runs of consecutive
+        sequences whose tables start with the same block, and the number of
+        leading whole blocks every member of the run shares."""
+        return shared_prefix_groups(self.block_tables, self.context_lens, self.block_size)
+
     def write_bytes(self) -> int:
         """Bytes one slot write reads plus writes (K and V of every new token)."""
         n = int((self.slot_mapping >= 0).sum())
         return 2 * 2 * n * self.num_kv_heads * self.head_dim * element_bytes(self.kv_dtype)
+
+
+def shared_prefix_groups(tables: np.ndarray, lens: np.ndarray, block_size: int):
+    """Runs of consecutive sequences that share leading blocks, for the
+    shared-prefix decode: (group_starts [G+1], prefix_blocks [G]) int32.
+    A run is a maximal set of consecutive sequences whose first table entry
+    is the same block; its prefix is the common leading part of their tables,
+    cut to the whole blocks inside every member's context."""
+    S = len(lens)
+    starts, pref = [0], []
+    s = 0
+    while s < S:
+        e = s + 1
+        nb0 = int(lens[s]) // block_size
+        while e < S and nb0 > 0 and int(lens[e]) // block_size > 0 and \
+                tables[e, 0] == tables[s, 0]:
+            e += 1
+        p = min(int(lens[i]) // block_size for i in range(s, e))
+        for i in range(s + 1, e):
+            same = tables[i, :p] == tables[s, :p]
+            p = int(np.argmin(same)) if not same.all() else p
+        pref.append(p if e - s > 1 else 0)
+        starts.append(e)
+        s = e
+    return np.array(starts, np.int32), np.array(pref, np.int32)
 
 
 def new_token_slot(table_row: np.ndarray, L: int, block_size: int) -> int:

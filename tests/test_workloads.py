@@ -126,3 +126,20 @@ def test_permute_and_contiguous_preserve_logical_content():
     nb = c.blocks_per_seq()
     starts = np.concatenate([[0], np.cumsum(nb)[:-1]])
     assert np.all(c.block_tables[:, 0] == starts)
+
+
+def test_shared_prefix_groups():
+    w = wl.make_config(4)
+    gs, pb = w.prefix_groups()
+    assert list(gs) == list(range(0, 129, 8)) and list(pb) == [128] * 16
+    tables = np.array([[5, 6, 7, 8], [5, 6, 9, 10], [5, 6, 7, 11], [3, 4, -1, -1], [1, 2, 0, -1]],
+                      np.int32)
+    lens = np.array([64, 60, 33, 20, 40], np.int32)
+    gs, pb = wl.shared_prefix_groups(tables, lens, 16)
+    # run 0..2 shares blocks 5, 6 (and 7 only between 0 and 2); sequence 2
+    # holds 2 whole blocks, so 2; the rest are singletons
+    assert list(gs) == [0, 3, 4, 5] and list(pb) == [2, 0, 0]
+    gs, pb = wl.shared_prefix_groups(tables[:3], np.array([64, 64, 64], np.int32), 16)
+    assert list(pb) == [2]
+    gs, pb = wl.shared_prefix_groups(tables[[0, 2]], np.array([64, 64], np.int32), 16)
+    assert list(pb) == [3]
