@@ -487,6 +487,214 @@ __device__ __forceinline__ const PA_CONST T* as_const(const T* p) {
   return (const PA_CONST T*)(const void PA_CONST*)(uintptr_t)p;
 }
 
+// ---------------------------------------------------------------------------
+// Shared-prefix kernel, bf16 KV.
+// ---------------------------------------------------------------------------
+
+// Query rows of one prefix item: two 16-column halves of the MFMA tiles.
+constexpr int kPrefixRows = 32;
+
+// LDS of the prefix kernel: per wave, (max, sum) and weighted sums of the 32 rows.
+template <int D, int W>
+__host__ __device__ constexpr int prefix_lds_floats() {
+  return 2 * W * kPrefixRows + W * kPrefixRows * (D + 4);
+}
+
+// Parallel samples of one prompt ("How does vLLM PagedAttention manage
+// Virtual Memory Pages ...", section "Key Technical Innovations", item 3)
+// hold the prompt's blocks once; this kernel reads each of those K/V tiles
+// once for all the sequences of a prefix item and all their query heads:
+// up to 32 query rows (sequence-major, head-minor) in two 16-column halves,
+//   S^T[16 tokens x 16 rows] = K[16 x D] * Q^T[D x 16]        per half
+//   O^T[16 d x 16 rows]     += V^T[16 d x 16] * P^T[16 x 16]  per half
+// so one tile feeds 32 rows' scores and weighted sums.  The streaming
+// kernel runs these items first (item bid, bid + NG, ... of workgroup bid),
+// then its own work list.  Work item = (prefix item, KV head); the W waves
+// take the item's blocks b0 + w,
+// b0 + w + W, ... with two tile buffers in flight, and their states are
+// merged through LDS in wave order.  The result of each sequence's rows is
+// stored as its partition state number `part` (prefix partitions precede
+// the sequence's own partitions), for merge_splits.  Prefix blocks are whole
+// and inside every member's context, so nothing is masked except blocks
+// whose id is outside the pool (which then contribute nothing).
+template <int D, int BS, int W>
+__device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem, int bid, int NG) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, quad = lane >> 4;
+  const int G = a.group, Hkv = a.num_kv_heads, Hq = a.num_heads;
+  const PA_CONST int32_t* ctrl = as_const(a.ws_ctrl);
+  const PA_CONST int32_t* pitems = as_const((const int32_t*)a.ws_pitems);
+  const PA_CONST int32_t* tables = as_const(a.tables);
+  const int total = ctrl[kCtrlPrefixItems] * Hkv;
+  const int pbp = ctrl[kCtrlPrefixPart];
+  float* sm_m = smem;
+  float* sm_l = smem + W * kPrefixRows;
+  float* sm_acc = smem + 2 * W * kPrefixRows;
+  const uint32_t tile_bytes = (uint32_t)BS * D * 2;
+  const LaneOff lo = lane_offsets<D, BS>(lane, G);
+  const char* kbase = (const char*)a.k_cache;
+  const char* vbase = (const char*)a.v_cache;
+
+  for (int item = bid; item < total; item += NG) {
+    const int e = item / Hkv;
+    const int kv = item - e * Hkv;
+    const int first = pitems[4 * e + 0], nseq = pitems[4 * e + 1];
+    const int part = pitems[4 * e + 2], P = pitems[4 * e + 3];
+    const int b0 = part * pbp, b1 = min(b0 + pbp, P);
+    const int rows = nseq * G;
+
+    // Query operands: row r = 16 * half + col is head r % G of sequence
+    // first + r / G; rows past the item's sequences read zeros.
+    bf16x8 qop[2][D / 32];
+    {
+      const uint32_t qbytes = (uint32_t)nseq * Hq * D * 2;
+      const __amdgpu_buffer_rsrc_t qr =
+          buffer_of((const char*)a.q + (int64_t)first * Hq * D * 2, qbytes);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = hh * 16 + col;
+        const uint32_t off = r < rows ? ((uint32_t)((r / G) * Hq + kv * G + r % G) * D + quad * 8) * 2
+                                      : qbytes;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          qop[hh][c] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off + c * 64, 0, 0));
+      }
+    }
+
+    float m[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
+    f32x4 acc[2][D / 16];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t trow = (int64_t)first * a.max_blocks;
+    // Loads of block j (of the first member's table) into t; positions past
+    // the item's blocks or with an id outside the pool read zeros.
+    auto load_blk = [&](Tile<D, BS>& t, int j, bool& has) {
+      int id = 0;
+      if (j < b1) id = tables[trow + j];
+      has = j < b1 && (unsigned)id < (unsigned)a.num_blocks;
+      const int64_t off = has ? ((int64_t)id * Hkv + kv) * tile_bytes : 0;
+      const uint32_t nb = has ? tile_bytes : 0;
+      load_tile<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo);
+    };
+
+    auto compute = [&](Tile<D, BS>& t, bool has) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x4 sc[Tile<D, BS>::SB];
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb) {
+          sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+            sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sb][c], qop[hh][c], sc[sb], 0, 0, 0);
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float x = has ? sc[sb][rr] * a.scale_log2 : kNegInf;
+            sc[sb][rr] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mnew = fmaxf(m[hh], mx);
+        const float mref = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = exp2_fast(m[hh] - mref);
+        m[hh] = mnew;
+        i16x4 pw[Tile<D, BS>::SB];
+        float psum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
+            pw[sb][rr] = (short)bits;
+            psum += bf16_bits_to_f32(bits);
+          }
+        lsum[hh] = lsum[hh] * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+          for (int i = 0; i < D / 16; ++i) acc[hh][i] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+          for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
+            acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[hh][i],
+                                                                   0, 0, 0);
+      }
+    };
+
+    // Two buffers in flight: every step issues the loads of the position
+    // two ahead, then computes the oldest one.
+    Tile<D, BS> t0, t1;
+    bool h0 = false, h1 = false;
+    int j = b0 + w;
+    load_blk(t0, j, h0);
+    for (;;) {
+      load_blk(t1, j + W, h1);
+      if (j >= b1) break;
+      compute(t0, h0);
+      j += W;
+      load_blk(t0, j + W, h0);
+      if (j >= b1) break;
+      compute(t1, h1);
+      j += W;
+    }
+
+    // Wave state -> LDS (row r of half hh is column col).
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float ls = lsum[hh];
+      ls += shfl_xor_f(ls, 16);
+      ls += shfl_xor_f(ls, 32);
+      const int r = hh * 16 + col;
+      if (quad == 0) {
+        sm_m[w * kPrefixRows + r] = m[hh];
+        sm_l[w * kPrefixRows + r] = ls;
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+        *reinterpret_cast<f32x4*>(&sm_acc[(w * kPrefixRows + r) * (D + 4) + i * 16 + quad * 4]) =
+            acc[hh][i];
+    }
+    __syncthreads();
+    // Merge the W wave states in wave order and store each member's rows as
+    // its partition state `part`.
+    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += 64 * W) {
+      const int r = idx / (D / 4);
+      const int d4 = idx - r * (D / 4);
+      float M = kNegInf;
+#pragma unroll
+      for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v * kPrefixRows + r]);
+      float lam = 0.f;
+      f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float mv = sm_m[v * kPrefixRows + r];
+        const float c = mv == kNegInf ? 0.f : exp2_fast(mv - M);
+        lam += sm_l[v * kPrefixRows + r] * c;
+        val += *reinterpret_cast<const f32x4*>(&sm_acc[(v * kPrefixRows + r) * (D + 4) + d4 * 4]) * c;
+      }
+      const int sq = first + r / G, g = r % G;
+      const int64_t row = (((int64_t)sq * Hkv + kv) * a.num_parts_max + part) * G + g;
+      *reinterpret_cast<f32x4*>(a.ws_acc + row * D + d4 * 4) = val;
+      if (d4 == 0) {
+        a.ws_ml[row * 2 + 0] = M;
+        a.ws_ml[row * 2 + 1] = lam;
+      }
+    }
+    __syncthreads();   // LDS is reused by the next item
+  }
+}
+
 // One work item as a wave sees it (every field is uniform across the wave).
 struct Desc {
   int s, h, L, b0, nparts, part;
@@ -507,7 +715,7 @@ struct Desc {
 // them and wait only for the buffer it uses.  After the last position of an
 // item each wave hands its state to the item's LDS slot; the last wave of
 // the workgroup to do so merges them and writes the result (see finish).
-template <int D, int BS, int W>
+template <int D, int BS, int W, bool PREFIX>
 __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
@@ -569,6 +777,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     return d;
   };
 
+  // Shared prefixes first: every wave of the workgroup takes part (the
+  // items end with barriers), and the LDS they use is free again after.
+  if constexpr (PREFIX) prefix_items<D, BS, W>(a, smem, bid, NG);
   if (bid >= total) return;          // no work for this workgroup at all
   if (threadIdx.x < kMaxLdsSlots) {
     s_count[threadIdx.x] = 0;
@@ -822,213 +1033,6 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared-prefix kernel, bf16 KV.
-// ---------------------------------------------------------------------------
-
-// Query rows of one prefix item: two 16-column halves of the MFMA tiles.
-constexpr int kPrefixRows = 32;
-
-// LDS of the prefix kernel: per wave, (max, sum) and weighted sums of the 32 rows.
-template <int D, int W>
-__host__ __device__ constexpr int prefix_lds_floats() {
-  return 2 * W * kPrefixRows + W * kPrefixRows * (D + 4);
-}
-
-// Parallel samples of one prompt ("How does vLLM PagedAttention manage
-// Virtual Memory Pages ...", section "Key Technical Innovations", item 3)
-// hold the prompt's blocks once; this kernel reads each of those K/V tiles
-// once for all the sequences of a prefix item and all their query heads:
-// up to 32 query rows (sequence-major, head-minor) in two 16-column halves,
-//   S^T[16 tokens x 16 rows] = K[16 x D] * Q^T[D x 16]        per half
-//   O^T[16 d x 16 rows]     += V^T[16 d x 16] * P^T[16 x 16]  per half
-// so one tile feeds 32 rows' scores and weighted sums.  Work item =
-// (prefix item, KV head); the W waves take the item's blocks b0 + w,
-// b0 + w + W, ... with two tile buffers in flight, and their states are
-// merged through LDS in wave order.  The result of each sequence's rows is
-// stored as its partition state number `part` (prefix partitions precede
-// the sequence's own partitions), for merge_splits.  Prefix blocks are whole
-// and inside every member's context, so nothing is masked except blocks
-// whose id is outside the pool (which then contribute nothing).
-template <int D, int BS, int W>
-__global__ __launch_bounds__(64 * W) void prefix_mfma_bf16(DecodeParams a) {
-  extern __shared__ float smem[];
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, quad = lane >> 4;
-  const int G = a.group, Hkv = a.num_kv_heads, Hq = a.num_heads;
-  const PA_CONST int32_t* ctrl = as_const(a.ws_ctrl);
-  const PA_CONST int32_t* pitems = as_const((const int32_t*)a.ws_pitems);
-  const PA_CONST int32_t* tables = as_const(a.tables);
-  const int total = ctrl[kCtrlPrefixItems] * Hkv;
-  const int pbp = ctrl[kCtrlPrefixPart];
-  float* sm_m = smem;
-  float* sm_l = smem + W * kPrefixRows;
-  float* sm_acc = smem + 2 * W * kPrefixRows;
-  const uint32_t tile_bytes = (uint32_t)BS * D * 2;
-  const LaneOff lo = lane_offsets<D, BS>(lane, G);
-  const char* kbase = (const char*)a.k_cache;
-  const char* vbase = (const char*)a.v_cache;
-
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int e = item / Hkv;
-    const int kv = item - e * Hkv;
-    const int first = pitems[4 * e + 0], nseq = pitems[4 * e + 1];
-    const int part = pitems[4 * e + 2], P = pitems[4 * e + 3];
-    const int b0 = part * pbp, b1 = min(b0 + pbp, P);
-    const int rows = nseq * G;
-
-    // Query operands: row r = 16 * half + col is head r % G of sequence
-    // first + r / G; rows past the item's sequences read zeros.
-    bf16x8 qop[2][D / 32];
-    {
-      const uint32_t qbytes = (uint32_t)nseq * Hq * D * 2;
-      const __amdgpu_buffer_rsrc_t qr =
-          buffer_of((const char*)a.q + (int64_t)first * Hq * D * 2, qbytes);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = hh * 16 + col;
-        const uint32_t off = r < rows ? ((uint32_t)((r / G) * Hq + kv * G + r % G) * D + quad * 8) * 2
-                                      : qbytes;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-          qop[hh][c] = __builtin_bit_cast(
-              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, off + c * 64, 0, 0));
-      }
-    }
-
-    float m[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
-    f32x4 acc[2][D / 16];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i) acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int64_t trow = (int64_t)first * a.max_blocks;
-    // Loads of block j (of the first member's table) into t; positions past
-    // the item's blocks or with an id outside the pool read zeros.
-    auto load_blk = [&](Tile<D, BS>& t, int j, bool& has) {
-      int id = 0;
-      if (j < b1) id = tables[trow + j];
-      has = j < b1 && (unsigned)id < (unsigned)a.num_blocks;
-      const int64_t off = has ? ((int64_t)id * Hkv + kv) * tile_bytes : 0;
-      const uint32_t nb = has ? tile_bytes : 0;
-      load_tile<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo);
-    };
-
-    auto compute = [&](Tile<D, BS>& t, bool has) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x4 sc[Tile<D, BS>::SB];
-#pragma unroll
-        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb) {
-          sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c)
-            sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sb][c], qop[hh][c], sc[sb], 0, 0, 0);
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const float x = has ? sc[sb][rr] * a.scale_log2 : kNegInf;
-            sc[sb][rr] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float mnew = fmaxf(m[hh], mx);
-        const float mref = mnew == kNegInf ? 0.f : mnew;
-        const float alpha = exp2_fast(m[hh] - mref);
-        m[hh] = mnew;
-        i16x4 pw[Tile<D, BS>::SB];
-        float psum = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
-            pw[sb][rr] = (short)bits;
-            psum += bf16_bits_to_f32(bits);
-          }
-        lsum[hh] = lsum[hh] * alpha + psum;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-          for (int i = 0; i < D / 16; ++i) acc[hh][i] *= alpha;
-        }
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-          for (int sb = 0; sb < Tile<D, BS>::SB; ++sb)
-            acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[hh][i],
-                                                                   0, 0, 0);
-      }
-    };
-
-    // Two buffers in flight: every step issues the loads of the position
-    // two ahead, then computes the oldest one.
-    Tile<D, BS> t0, t1;
-    bool h0 = false, h1 = false;
-    int j = b0 + w;
-    load_blk(t0, j, h0);
-    for (;;) {
-      load_blk(t1, j + W, h1);
-      if (j >= b1) break;
-      compute(t0, h0);
-      j += W;
-      load_blk(t0, j + W, h0);
-      if (j >= b1) break;
-      compute(t1, h1);
-      j += W;
-    }
-
-    // Wave state -> LDS (row r of half hh is column col).
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float ls = lsum[hh];
-      ls += shfl_xor_f(ls, 16);
-      ls += shfl_xor_f(ls, 32);
-      const int r = hh * 16 + col;
-      if (quad == 0) {
-        sm_m[w * kPrefixRows + r] = m[hh];
-        sm_l[w * kPrefixRows + r] = ls;
-      }
-#pragma unroll
-      for (int i = 0; i < D / 16; ++i)
-        *reinterpret_cast<f32x4*>(&sm_acc[(w * kPrefixRows + r) * (D + 4) + i * 16 + quad * 4]) =
-            acc[hh][i];
-    }
-    __syncthreads();
-    // Merge the W wave states in wave order and store each member's rows as
-    // its partition state `part`.
-    for (int idx = threadIdx.x; idx < rows * (D / 4); idx += 64 * W) {
-      const int r = idx / (D / 4);
-      const int d4 = idx - r * (D / 4);
-      float M = kNegInf;
-#pragma unroll
-      for (int v = 0; v < W; ++v) M = fmaxf(M, sm_m[v * kPrefixRows + r]);
-      float lam = 0.f;
-      f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < W; ++v) {
-        const float mv = sm_m[v * kPrefixRows + r];
-        const float c = mv == kNegInf ? 0.f : exp2_fast(mv - M);
-        lam += sm_l[v * kPrefixRows + r] * c;
-        val += *reinterpret_cast<const f32x4*>(&sm_acc[(v * kPrefixRows + r) * (D + 4) + d4 * 4]) * c;
-      }
-      const int sq = first + r / G, g = r % G;
-      const int64_t row = (((int64_t)sq * Hkv + kv) * a.num_parts_max + part) * G + g;
-      *reinterpret_cast<f32x4*>(a.ws_acc + row * D + d4 * 4) = val;
-      if (d4 == 0) {
-        a.ws_ml[row * 2 + 0] = M;
-        a.ws_ml[row * 2 + 1] = lam;
-      }
-    }
-    __syncthreads();   // LDS is reused by the next item
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Vector-ALU kernel (fp32 KV; also bf16 when asked).
 // ---------------------------------------------------------------------------
 
@@ -1155,41 +1159,44 @@ __global__ __launch_bounds__(256) void merge_splits(DecodeParams a) {
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
   constexpr int kBatch = 4;
   const int Hkv = a.num_kv_heads, G = a.group;
-  const int total = a.ws_ctrl[kCtrlSplits] * Hkv;
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int2 e = a.ws_split[item / Hkv];
+  // One thread per (split sequence, KV head, query head of the group, 4 features).
+  const int per_seq = Hkv * G * (D / 4);
+  const int64_t total = (int64_t)a.ws_ctrl[kCtrlSplits] * per_seq;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int e_idx = (int)(idx / per_seq);
+    const int rem = (int)(idx - (int64_t)e_idx * per_seq);
+    const int h = rem / (G * (D / 4));
+    const int g = (rem / (D / 4)) % G;
+    const int d4 = rem % (D / 4);
+    const int2 e = a.ws_split[e_idx];
     const int s = e.x, nparts = e.y;
-    const int h = item % Hkv;
     const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
-    for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
-      const int g = idx / (D / 4);
-      const int d4 = idx - g * (D / 4);
-      float M = kNegInf, lam = 0.f;
-      f4 val = {0.f, 0.f, 0.f, 0.f};
-      for (int p0 = 0; p0 < nparts; p0 += kBatch) {
-        float mp[kBatch], lp[kBatch];
-        f4 ap[kBatch];
+    float M = kNegInf, lam = 0.f;
+    f4 val = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < nparts; p0 += kBatch) {
+      float mp[kBatch], lp[kBatch];
+      f4 ap[kBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int64_t row = (prow + min(p0 + j, nparts - 1)) * G + g;
-          mp[j] = a.ws_ml[row * 2];
-          lp[j] = a.ws_ml[row * 2 + 1];
-          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          if (p0 + j >= nparts) break;
-          const float Mn = fmaxf(M, mp[j]);
-          if (Mn == kNegInf) continue;        // nothing live yet
-          const float cold = exp2_fast(M - Mn), cnew = exp2_fast(mp[j] - Mn);
-          lam = lam * cold + lp[j] * cnew;
-          val = val * cold + ap[j] * cnew;
-          M = Mn;
-        }
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t row = (prow + min(p0 + j, nparts - 1)) * G + g;
+        mp[j] = a.ws_ml[row * 2];
+        lp[j] = a.ws_ml[row * 2 + 1];
+        ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
       }
-      const f4 o = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) = o;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (p0 + j >= nparts) break;
+        const float Mn = fmaxf(M, mp[j]);
+        if (Mn == kNegInf) continue;        // nothing live yet
+        const float cold = exp2_fast(M - Mn), cnew = exp2_fast(mp[j] - Mn);
+        lam = lam * cold + lp[j] * cnew;
+        val = val * cold + ap[j] * cnew;
+        M = Mn;
+      }
     }
+    const f4 o = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) = o;
   }
 }
 
@@ -1251,9 +1258,15 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   // The adaptive partition keeps one partition at most 2/W of a workgroup's
   // share, so each wave's part of it is at most half a wave's share.
   if (p.balance) p.balance = kWaves / 2;
+  const bool prefix = p.num_groups > 0;   // bf16 matrix-core kernel only (checked by the API)
   if (type == KvType::BF16 && !vector_alu) {
-    kernel = (const void*)decode_mfma_bf16<D, BS, kWaves>;
+    kernel = prefix ? (const void*)decode_mfma_bf16<D, BS, kWaves, true>
+                    : (const void*)decode_mfma_bf16<D, BS, kWaves, false>;
     smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
+    if (prefix) {
+      const size_t pre = (size_t)prefix_lds_floats<D, kWaves>() * 4;
+      smem = smem > pre ? smem : pre;
+    }
   } else if (type == KvType::BF16) {
     kernel = (const void*)decode_valu<uint16_t, D, BS, kWaves>;
     smem = smem_bytes<D>(p0.group, true, BS, 0, 0);
@@ -1270,21 +1283,13 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.num_groups > 0) {
-    // Shared prefixes (bf16, matrix cores only; checked by the API).
-    const void* pk = (const void*)prefix_mfma_bf16<D, BS, kWaves>;
-    const size_t psmem = (size_t)prefix_lds_floats<D, kWaves>() * 4;
-    const int pres = resident_workgroups(pk, threads, psmem);
-    if (pres <= 0) return hipErrorInvalidDeviceFunction;
-    const int pgrid = (int)(max_items < pres ? max_items : pres);
-    hipLaunchKernelGGL((prefix_mfma_bf16<D, BS, kWaves>), dim3(pgrid), dim3(threads), psmem,
-                       stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
-  if (type == KvType::BF16 && !vector_alu)
-    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves>), dim3(p.decode_grid), dim3(threads),
-                       smem, stream, p);
+  if (type == KvType::BF16 && !vector_alu && prefix)
+    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, true>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else if (type == KvType::BF16 && !vector_alu)
+    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
   else if (type == KvType::BF16)
     hipLaunchKernelGGL((decode_valu<uint16_t, D, BS, kWaves>), dim3(p.decode_grid),
                        dim3(threads), smem, stream, p);
@@ -1295,8 +1300,11 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
   if (p.num_parts_max <= 1) return hipSuccess;
-  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
-  const unsigned mgrid = (unsigned)(pairs < 256 ? pairs : 256);
+  // Enough threads for every (sequence, head, 4 features) of a full batch of
+  // split sequences, up to 4 workgroups per CU; the kernel loops past that.
+  const int64_t threads_needed = (int64_t)p.num_seqs * p.num_heads * (D / 4);
+  const int64_t mblocks = (threads_needed + 255) / 256;
+  const unsigned mgrid = (unsigned)(mblocks < 1024 ? mblocks : 1024);
   hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
