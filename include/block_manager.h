@@ -116,6 +116,16 @@ int pa_bm_swap_in(pa_block_manager* bm, const int64_t* seqs, int32_t n, int32_t*
 int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t n,
                        int32_t* tables, int32_t stride, int32_t* context_lens);
 
+/* Groups for pa_decode_shared_prefix over the batch seqs[0..n-1] (device
+ * sequences, in the order the batch lists them): maximal runs of consecutive
+ * sequences whose tables start with the same block, e.g. samples forked from
+ * one prompt and listed together.  group_starts [n + 1] receives the run
+ * boundaries (group g = batch entries group_starts[g] .. group_starts[g+1]-1),
+ * prefix_blocks [n] the number of leading whole blocks every member of the run
+ * holds in common (0 for a run of one), *num_groups the number of runs. */
+int pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seqs, int32_t n,
+                        int32_t* group_starts, int32_t* prefix_blocks, int32_t* num_groups);
+
 /* One sequence: its table (NULL, or room for max_blocks_per_seq entries),
  * length, number of blocks and pool (PA_POOL_DEVICE / PA_POOL_HOST). */
 int pa_bm_sequence(const pa_block_manager* bm, int64_t seq, int32_t* table, int32_t* length,

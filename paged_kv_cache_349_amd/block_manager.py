@@ -43,6 +43,7 @@ _SIGNATURES = {
     "pa_bm_swap_out": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32)]),
     "pa_bm_swap_in": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, ctypes.POINTER(_i32)]),
     "pa_bm_block_tables": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _vp]),
+    "pa_bm_prefix_groups": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, ctypes.POINTER(_i32)]),
     "pa_bm_sequence": (ctypes.c_int, [_vp, _i64, _vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                                       ctypes.POINTER(_i32)]),
     "pa_bm_num_free": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
@@ -180,6 +181,16 @@ class BlockManager:
             raise ValueError("out arrays: int32 [n, stride] and [n]")
         _call(_lib().pa_bm_block_tables(self._h, _ptr(ids), ids.size, _ptr(t), stride, _ptr(lens)))
         return t, lens
+
+    def prefix_groups(self, seqs):
+        """(group_starts [G+1], prefix_blocks [G]) int32 for pa_decode_shared_prefix."""
+        ids = _ids(seqs)
+        gs = np.empty(ids.size + 1, np.int32)
+        pb = np.empty(max(ids.size, 1), np.int32)
+        ng = _i32(0)
+        _call(_lib().pa_bm_prefix_groups(self._h, _ptr(ids), ids.size, _ptr(gs), _ptr(pb),
+                                         ctypes.byref(ng)))
+        return gs[:ng.value + 1].copy(), pb[:ng.value].copy()
 
     def sequence(self, seq):
         """(table, length, number of blocks, pool) of one sequence."""

@@ -350,6 +350,47 @@ int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t 
   return succeed();
 }
 
+int pa_bm_prefix_groups(const pa_block_manager* bm, const int64_t* seqs, int32_t n,
+                        int32_t* group_starts, int32_t* prefix_blocks, int32_t* num_groups) {
+  if (!bm || !num_groups || n < 0 || !group_starts || (n > 0 && (!seqs || !prefix_blocks)))
+    return fail(PA_ERR_INVALID_ARG, "null pointer or n=%d < 0", n);
+  std::vector<const Seq*> list((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = bm->find(seqs[i]);
+    if (!s) return fail(PA_ERR_INVALID_ARG, "unknown sequence %lld", (long long)seqs[i]);
+    if (s->pool != PA_POOL_DEVICE)
+      return fail(PA_ERR_INVALID_ARG, "sequence %lld is swapped out", (long long)seqs[i]);
+    list[(size_t)i] = s;
+  }
+  const int32_t bs = bm->block_size;
+  auto whole = [&](const Seq* s) {
+    const int32_t w = s->len / bs;
+    return w < (int32_t)s->table.size() ? w : (int32_t)s->table.size();
+  };
+  int32_t g = 0;
+  group_starts[0] = 0;
+  for (int32_t i = 0; i < n;) {
+    const Seq* a = list[(size_t)i];
+    int32_t p = whole(a);
+    int32_t e = i + 1;
+    while (p > 0 && e < n && whole(list[(size_t)e]) > 0 &&
+           list[(size_t)e]->table[0] == a->table[0])
+      ++e;
+    for (int32_t k = i + 1; k < e; ++k) {
+      const Seq* b = list[(size_t)k];
+      const int32_t lim = p < whole(b) ? p : whole(b);
+      int32_t j = 0;
+      while (j < lim && b->table[(size_t)j] == a->table[(size_t)j]) ++j;
+      p = j;
+    }
+    prefix_blocks[g] = e - i > 1 ? p : 0;
+    group_starts[++g] = e;
+    i = e;
+  }
+  *num_groups = g;
+  return succeed();
+}
+
 int pa_bm_sequence(const pa_block_manager* bm, int64_t seq, int32_t* table, int32_t* length,
                    int32_t* num_blocks, int32_t* pool) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "null manager");

@@ -217,3 +217,33 @@ def test_cpp_stats_match_waste_measures():
     assert st["device_blocks_shared"] == 128
     assert abs(st["device_internal_waste"] -
                obm.waste_paged(lens, 16, shared_tokens=7 * 2048, shared_blocks=7 * 128)) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cpp_prefix_groups_match_generator_rule(seed):
+    """The manager's groups equal the rule applied to its own tables."""
+    from paged_kv_cache_349_amd import workloads as wl
+    rng = np.random.default_rng(seed)
+    bs = int(rng.choice([4, 16]))
+    m = BlockManager(4000, 0, bs, 200, device_free_order=rng.permutation(4000))
+    batch, nxt = [], 0
+    for _ in range(6):
+        root = nxt
+        m.add(root, int(rng.integers(0, 6 * bs)))
+        nxt += 1
+        kids = [root]
+        for _ in range(int(rng.integers(0, 5))):
+            m.fork(root, nxt)
+            kids.append(nxt)
+            nxt += 1
+        for _ in range(int(rng.integers(0, 3 * bs))):
+            m.append_batch(kids)
+        batch += kids
+    order = list(batch)
+    if seed % 2:                                  # interleave some groups
+        order[1], order[-1] = order[-1], order[1]
+    gs, pb = m.prefix_groups(order)
+    tables, lens = m.tables(order)
+    gs2, pb2 = wl.shared_prefix_groups(tables, lens, bs)
+    assert list(gs) == list(gs2) and list(pb) == list(pb2)
+    assert gs[0] == 0 and gs[-1] == len(order)

@@ -215,6 +215,15 @@ def test_serving_loop_with_sharing_cow_and_swap(dt):
         err = float(np.abs(out.cpu().numpy() - ref).max())
         _say(f"  step {step}: {len(active)} seqs, {len(cs)} copies, max-abs err {err:.2e}")
         assert err <= TOL[dt], (step, err)
+        if dt == "bf16":
+            # the same step through the shared-prefix path, groups from the manager
+            gs, pb = m.prefix_groups(active)
+            assert pb.max() == prompt // bs
+            out2 = torch.full_like(out, float("nan"))
+            pa.decode_shared_prefix(out2, _dev(q, dt), kd, vd, _i32(tables), _i32(lens),
+                                    _i32(gs), _i32(pb), float(scale), bs)
+            torch.cuda.synchronize()
+            assert float(np.abs(out2.cpu().numpy() - ref).max()) <= TOL[dt], step
     assert np.array_equal(_raw(_np(hkd, dt)), _raw(hk))
     st_ = m.stats()
     # the full prompt blocks stay shared by the 6 that never left, and the two
