@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--block-size 16|32]
 
-One step = one pa_write_kv (the new token of every sequence goes into its
-slot) + one pa_decode (single-query attention of every sequence over the
-paged pool), on one HIP stream, over the large-batch GQA workload:
+One step = the slot write (the new token of every sequence goes into its
+slot) + decode (single-query attention of every sequence over the paged
+pool), on one HIP stream, issued as one pa_decode_step call (also timed as
+pa_write_kv + pa_decode), over the large-batch GQA workload:
 256 sequences, context lengths lognormal(6.9, 0.6) clipped to [16, 8192],
 64 query heads / 8 KV heads, head_dim 128, block size 16, bf16 K/V/q, fp32
 output, a shuffled pool with 3% free blocks.  Inputs are seeded synthetic
@@ -297,17 +298,31 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    def step():
+        pa.decode_step(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping, d.out, d.q,
+                       d.block_tables, d.context_lens, float(w.scale), w.block_size)
+
+    fused = not args.shared_prefix and args.partition_tokens == 0
+    for _ in range(args.warmup if fused else 0):
+        step()
+
+    def timed_loop(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
     K = args.steps
     # Throughput: K steps back to back, nothing else on the stream, one
-    # synchronisation on each side.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        write()
-        decode()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log(f"timed {K} steps: {wall * 1e6 / K:.1f} us/step")
+    # synchronisation on each side.  A step is pa_decode_step (the write and
+    # the decode, the write sharing the planner's launch); the same steps as
+    # two calls (pa_write_kv, pa_decode) are timed the same way.
+    wall_sep = timed_loop(lambda: (write(), decode()))
+    wall = timed_loop(step) if fused else wall_sep
+    log(f"timed {K} steps: {wall * 1e6 / K:.1f} us/step"
+        + (f" (as two calls: {wall_sep * 1e6 / K:.1f} us/step)" if fused else ""))
 
     # Breakdown: the same K steps again with HIP events around each call and
     # the library's events around the attention kernel.
@@ -361,6 +376,8 @@ def main() -> int:
             "seed": args.seed if args.seed is not None else wl.SEED_BASE + args.config,
         },
         "seq_steps_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "step_call": "pa_decode_step" if fused else "pa_write_kv + pa_decode",
+        "ms_per_step_two_calls": round(wall_sep * 1e3 / K, 5),
         "pct_hbm_peak_step": round(100 * (alg_bytes + w.write_bytes()) / (ms_per_step * 1e-3) /
                                    (HBM_PEAK_GBPS * 1e9), 2),
         "decode_us": {"mean": round(dec_mean, 2), "median": round(dec_med, 2),

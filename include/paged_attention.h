@@ -86,6 +86,23 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
                 void* stream);
 
 /*
+ * One decode step: pa_write_kv followed by pa_decode, in one call, with the
+ * same results (bit for bit) as the two calls made in that order on
+ * `stream`.  The slot write and the decode planner do not depend on each
+ * other, so they run in one launch; the step takes one launch less.
+ * Arguments as in pa_write_kv (k_new, v_new, slot_mapping, num_tokens) and
+ * pa_decode (the rest); the workspace is pa_decode's.  Argument errors are
+ * reported before anything is launched.  Either part may be empty
+ * (num_tokens == 0 or num_seqs == 0).
+ */
+int pa_decode_step(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int32_t* slot_mapping, int32_t num_tokens, float* out, const void* q,
+                   const int32_t* block_tables, const int32_t* context_lens, float scale,
+                   int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks,
+                   int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Copy-on-write block copies inside one pool.  For i in [0, num_pairs):
  *   block dst_blocks[i] := block src_blocks[i]
  * in both k_cache and v_cache (all KV heads, all block_size positions; raw

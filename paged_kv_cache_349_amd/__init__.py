@@ -39,6 +39,8 @@ _SIGNATURES = {
                                    _c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp] + [_c_int] * 6 + [_vp]),
     "pa_swap_blocks": (ctypes.c_int, [_vp] * 6 + [_c_int] * 7 + [_vp]),
+    "pa_decode_step": (ctypes.c_int, [_vp] * 5 + [_c_int] + [_vp] * 4 + [ctypes.c_float] +
+                       [_c_int] * 8 + [_vp, ctypes.c_size_t, _vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 7),
     "pa_decode_workspace_bytes_ex": (ctypes.c_size_t, [_c_int] * 8),
     "pa_decode_partition_tokens": (_c_int, [_c_int] * 4),
@@ -248,6 +250,42 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     return out
 
 
+def decode_step(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tables, context_lens,
+                scale, block_size, stream=None, *, workspace=None):
+    """write_kv(...) then decode(...) in one call (the write shares the planner's launch)."""
+    torch = _torch()
+    lib = load_library()
+    dev = _on_gpu(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tables,
+                  context_lens)
+    NB, Hkv, bs, D = _pool_shape(k_cache, v_cache)
+    _need(bs == block_size, f"block_size={block_size} but k_cache has {bs}")
+    _need(k_new.dtype == v_new.dtype == k_cache.dtype, "dtype mismatch")
+    _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1, "slot_mapping: int32 [T]")
+    T = slot_mapping.shape[0]
+    _need(tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D),
+          "k_new/v_new must be [T, Hkv, D]")
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
+    S, Hq, _ = q.shape
+    _need(q.dtype == k_cache.dtype, "q and caches must share a dtype")
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, D), "out: float32 [S, Hq, D]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens: int32 [S]")
+    code = _dtype_code(k_cache)
+    max_blocks = block_tables.shape[1]
+    need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code)
+    sh = _stream_handle(dev, stream)
+    if workspace is None:
+        workspace = _workspace(dev, sh, need)
+    _check(lib.pa_decode_step(
+        k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+        slot_mapping.data_ptr(), T, out.data_ptr(), q.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), float(scale), bs, S, Hq, Hkv, D, max_blocks, NB, code,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), sh))
+    return out
+
+
 def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
                          prefix_blocks, scale, block_size, stream=None, *, workspace=None,
                          partition_tokens=0):
@@ -300,5 +338,5 @@ def kernel_timing_end():
     return ms.value, n.value
 
 
-__all__ = ["write_kv", "decode", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+__all__ = ["write_kv", "decode", "decode_step", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
            "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]

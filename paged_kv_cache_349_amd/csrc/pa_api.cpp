@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "pa_internal.h"
+#include "pa_write_body.h"
 
 namespace {
 thread_local char g_last_error[512];
@@ -145,7 +146,8 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
                          int32_t num_blocks, int32_t kv_dtype, void* workspace,
                          size_t workspace_bytes, int32_t partition_tokens, int32_t flags,
                          const int32_t* group_starts, const int32_t* prefix_blocks,
-                         int32_t num_groups, bool prefix, void* stream) {
+                         int32_t num_groups, bool prefix, void* stream,
+                         const pa::WriteArgs* write = nullptr) {
   if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
@@ -232,7 +234,7 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
   const auto ev = next_timing_events();
   hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
                                    (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream,
-                                   ev.first, ev.second);
+                                   ev.first, ev.second, write);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -255,10 +257,12 @@ const char* pa_status_string(int32_t status) {
 
 const char* pa_last_error(void) { return g_last_error; }
 
-int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
-                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
-                void* stream) {
+// Argument checks of a slot write; PA_OK means it may be launched (a write
+// of 0 tokens launches nothing).
+static int check_write(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t kv_dtype) {
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
   if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
@@ -267,14 +271,54 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
                 "sizes must be positive (num_blocks=%d num_kv_heads=%d head_dim=%d block_size=%d)",
                 num_blocks, num_kv_heads, head_dim, block_size);
   if (head_dim > 1024) return fail(PA_ERR_UNSUPPORTED, "head_dim=%d > 1024", head_dim);
-  if (num_tokens == 0) return ok();
-  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+  if (num_tokens > 0 && (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping))
     return fail(PA_ERR_INVALID_ARG, "null device pointer with num_tokens=%d", num_tokens);
+  return PA_OK;
+}
+
+int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                void* stream) {
+  const int st = check_write(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                             num_blocks, num_kv_heads, head_dim, block_size, kv_dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens == 0) return ok();
   hipError_t e = pa::launch_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
                                      num_blocks, num_kv_heads, head_dim, block_size,
                                      (pa::KvType)kv_dtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "write_kv launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int pa_decode_step(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                   const int32_t* slot_mapping, int32_t num_tokens, float* out, const void* q,
+                   const int32_t* block_tables, const int32_t* context_lens, float scale,
+                   int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t num_blocks,
+                   int32_t kv_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_write(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                             num_blocks, num_kv_heads, head_dim, block_size, kv_dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens == 0 || num_seqs == 0) {
+    // Nothing to share a launch with: the plain calls.  Decode goes first (it
+    // launches nothing when num_seqs == 0), so that a failing step launches
+    // nothing.
+    const int d = pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                            block_size, num_seqs, num_heads, num_kv_heads, head_dim,
+                            max_blocks_per_seq, num_blocks, kv_dtype, workspace, workspace_bytes,
+                            stream);
+    if (d != PA_OK || num_tokens == 0) return d;
+    return pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_blocks,
+                       num_kv_heads, head_dim, block_size, kv_dtype, stream);
+  }
+  const pa::WriteArgs w =
+      pa::make_write_args(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_blocks,
+                          num_kv_heads, head_dim, block_size, (pa::KvType)kv_dtype);
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, nullptr, nullptr,
+                       0, false, stream, &w);
 }
 
 static int copy_blocks_common(const char* what, void* dst_k, void* dst_v, const void* src_k,

@@ -53,6 +53,7 @@
 #include <tuple>
 
 #include "pa_internal.h"
+#include "pa_write_body.h"
 
 namespace pa {
 namespace {
@@ -115,7 +116,7 @@ constexpr int kPartChoices = 8;
 
 constexpr int kLensCached = 8192;   // context lengths the planner keeps in LDS
 
-__global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
+__device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size) {
   __shared__ int lens_c[kLensCached];
   __shared__ int start_c[kLensCached];   // shared-prefix blocks per sequence
   __shared__ int cls_off[kTailClasses];
@@ -296,6 +297,23 @@ __global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_siz
     __syncthreads();
     if (tid == 0) a.ws_ctrl[kCtrlPrefixItems] = npitems;
   }
+}
+
+// The planner alone, or the planner in workgroup 0 and a slot write in the
+// others (the step's write and plan are independent, so they share a launch).
+__global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
+  plan_body(a, block_size);
+}
+
+template <typename E>
+__global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, int block_size,
+                                                       WriteArgs w) {
+  if (blockIdx.x == 0) {
+    plan_body(a, block_size);
+    return;
+  }
+  write_elements<E>(w, (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x,
+                    (int64_t)(gridDim.x - 1) * 1024);
 }
 
 struct Item {
@@ -1265,7 +1283,8 @@ int resident_workgroups(const void* kernel, int threads, size_t smem) {
 
 template <int D, int BS>
 hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_alu,
-                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after) {
+                               hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after,
+                               const WriteArgs* write) {
   const int threads = 64 * kWaves;
   const void* kernel;
   size_t smem;
@@ -1296,7 +1315,17 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   p.decode_grid = (int)(max_items < resident ? max_items : resident);
 
   p.prefix_rows = kPrefixRows;
-  hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
+  if (write && write->total > 0) {
+    int64_t wblocks = (write->total + 1023) / 1024;
+    if (wblocks > 4096) wblocks = 4096;   // grid-stride loop covers the rest
+    const dim3 grid((unsigned)(1 + wblocks));
+    if (write->elem_bytes == 2)
+      hipLaunchKernelGGL(write_and_plan<uint16_t>, grid, dim3(1024), 0, stream, p, BS, *write);
+    else
+      hipLaunchKernelGGL(write_and_plan<uint32_t>, grid, dim3(1024), 0, stream, p, BS, *write);
+  } else {
+    hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
@@ -1335,15 +1364,15 @@ bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t
 
 hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
                          int32_t block_size, bool vector_alu, hipStream_t stream,
-                         hipEvent_t ev_before, hipEvent_t ev_after) {
+                         hipEvent_t ev_before, hipEvent_t ev_after, const WriteArgs* write) {
   if (head_dim == 64 && block_size == 16)
-    return launch_decode_shape<64, 16>(p, type, vector_alu, stream, ev_before, ev_after);
+    return launch_decode_shape<64, 16>(p, type, vector_alu, stream, ev_before, ev_after, write);
   if (head_dim == 64 && block_size == 32)
-    return launch_decode_shape<64, 32>(p, type, vector_alu, stream, ev_before, ev_after);
+    return launch_decode_shape<64, 32>(p, type, vector_alu, stream, ev_before, ev_after, write);
   if (head_dim == 128 && block_size == 16)
-    return launch_decode_shape<128, 16>(p, type, vector_alu, stream, ev_before, ev_after);
+    return launch_decode_shape<128, 16>(p, type, vector_alu, stream, ev_before, ev_after, write);
   if (head_dim == 128 && block_size == 32)
-    return launch_decode_shape<128, 32>(p, type, vector_alu, stream, ev_before, ev_after);
+    return launch_decode_shape<128, 32>(p, type, vector_alu, stream, ev_before, ev_after, write);
   return hipErrorInvalidValue;
 }
 

@@ -69,6 +69,13 @@ enum class KvType { F32 = 0, BF16 = 1 };
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int succeed();
 
+struct WriteArgs;   // pa_write_body.h
+
+WriteArgs make_write_args(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          const int32_t* slots, int32_t num_tokens, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          KvType type);
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t num_tokens, int32_t num_blocks,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -84,9 +91,13 @@ hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const
 // Returns hipErrorInvalidValue for a (type, D, BS) combination without a kernel.
 // Non-null events are recorded on `stream` right before and right after the
 // attention kernel (not the planner or the merge), for kernel timing.
+// A non-null `write` is a slot write done in the planner's launch (its
+// workgroups other than the planner's), so the whole step takes one launch
+// less; the write and the plan are independent.
 hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
                          int32_t block_size, bool vector_alu, hipStream_t stream,
-                         hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
+                         hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
+                         const WriteArgs* write = nullptr);
 
 bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t group);
 

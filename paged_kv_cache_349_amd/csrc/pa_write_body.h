@@ -1,0 +1,51 @@
+// Slot-write element loop shared by the write kernel and the fused
+// write + plan kernel (device code; included by .hip sources only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace pa {
+
+// Arguments of one slot write (device pointers).
+struct WriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  int64_t total;        // num_tokens * num_kv_heads * head_dim elements
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_slots;    // num_blocks * block_size
+  int32_t elem_bytes;   // 2 (bf16) or 4 (fp32)
+};
+
+// Elements first, first + stride, ... of the write: one per (token, kv head,
+// feature).  Reads of k_new/v_new and the K-cache writes are contiguous along
+// the feature; V-cache writes stride by block_size elements because a V tile
+// keeps each feature's tokens together.  Raw bits are copied (uint16 / uint32).
+template <typename E>
+__device__ __forceinline__ void write_elements(const WriteArgs& w, int64_t first, int64_t stride) {
+  E* __restrict__ kc = (E*)w.k_cache;
+  E* __restrict__ vc = (E*)w.v_cache;
+  const E* __restrict__ kn = (const E*)w.k_new;
+  const E* __restrict__ vn = (const E*)w.v_new;
+  for (int64_t i = first; i < w.total; i += stride) {
+    const int32_t d = (int32_t)(i % w.head_dim);
+    const int64_t th = i / w.head_dim;
+    const int32_t h = (int32_t)(th % w.num_kv_heads);
+    const int64_t t = th / w.num_kv_heads;
+    const int64_t slot = w.slots[t];
+    if (slot < 0 || slot >= w.num_slots) continue;  // padding token, or out of the pool
+    const int64_t b = slot / w.block_size;
+    const int32_t o = (int32_t)(slot % w.block_size);
+    const int64_t tile = b * w.num_kv_heads + h;
+    kc[(tile * w.block_size + o) * w.head_dim + d] = kn[i];
+    vc[(tile * w.head_dim + d) * w.block_size + o] = vn[i];
+  }
+}
+
+}  // namespace pa

@@ -183,3 +183,15 @@ def test_shared_prefix_workspace_and_errors(lib):
     assert call(1, -1) == 1
     assert call(1, 1, S=9000) == 2    # more sequences than the planner keeps
     assert call(1, 1, S=0) == 0       # empty batch
+
+
+def test_decode_step_argument_errors(lib):
+    FAKE = 1 << 40
+    def call(T=2, S=4, dt=1, Hq=8, ws=1 << 30):
+        return lib.pa_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, T, FAKE, FAKE, FAKE, FAKE, 0.5, 16,
+                                  S, Hq, 2, 128, 4, 64, dt, FAKE, ws, None)
+    assert call(T=-1) == 1
+    assert call(dt=5) == 2
+    assert call(Hq=7) == 1          # Hq % Hkv
+    assert call(ws=16) == 3         # workspace too small: nothing launched
+    assert call(T=0, S=0) == 0      # empty step

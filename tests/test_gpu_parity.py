@@ -234,3 +234,52 @@ def test_kernel_timing_events():
     assert n == 2 and ms > 0.0
     with pytest.raises(ValueError):
         pa.kernel_timing_end()
+
+
+@pytest.mark.parametrize("cfg,bs", [(1, None), (2, None), (5, 32)])
+def test_decode_step_matches_separate_calls(cfg, bs):
+    """decode_step == write_kv then decode, bit for bit (pool and output)."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    _say(f"decode_step cfg {cfg} bs {bs}")
+    w = wl.make_config(cfg, block_size=bs, num_seqs=None if cfg != 5 else 64)
+    a, b = upload(w), upload(w)
+    pa.write_kv(a.k_cache, a.v_cache, a.k_new, a.v_new, a.slot_mapping)
+    pa.decode(a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, float(w.scale),
+              w.block_size)
+    pa.decode_step(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.out, b.q,
+                   b.block_tables, b.context_lens, float(w.scale), w.block_size)
+    torch.cuda.synchronize()
+    _assert_no_abort()
+    for x, y in ((a.k_cache, b.k_cache), (a.v_cache, b.v_cache)):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+
+
+def test_decode_step_empty_parts():
+    """A step with no new tokens decodes; a step with no sequences only writes."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    w = wl.make_config(1)
+    d = upload(w)
+    empty_i = torch.zeros(0, dtype=torch.int32, device="cuda:0")
+    empty_kv = torch.zeros((0,) + tuple(d.k_new.shape[1:]), dtype=d.k_new.dtype, device="cuda:0")
+    pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+    pa.decode_step(d.k_cache, d.v_cache, empty_kv, empty_kv, empty_i, d.out, d.q, d.block_tables,
+                   d.context_lens, float(w.scale), w.block_size)
+    torch.cuda.synchronize()
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, 16, "f32")
+    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL["f32"]
+    e = upload(w)
+    q0 = torch.zeros((0,) + tuple(e.q.shape[1:]), dtype=e.q.dtype, device="cuda:0")
+    out0 = torch.zeros((0,) + tuple(e.out.shape[1:]), dtype=torch.float32, device="cuda:0")
+    t0 = torch.zeros((0, e.block_tables.shape[1]), dtype=torch.int32, device="cuda:0")
+    pa.decode_step(e.k_cache, e.v_cache, e.k_new, e.v_new, e.slot_mapping, out0, q0, t0, empty_i,
+                   float(w.scale), w.block_size)
+    torch.cuda.synchronize()
+    from paged_kv_cache_349_amd.device_io import torch_to_np
+    assert np.array_equal(torch_to_np(e.k_cache, "f32").view(np.uint32), k_ref.view(np.uint32))
