@@ -77,6 +77,51 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def bench_ceilings(w, d, dev, stream, kern_mean_us):
+    """Empirical read ceilings on this GPU, for the roofline's context:
+    a contiguous read of the whole K and V pools, and a read of exactly the
+    decode's live K/V tiles through the block tables (sequence, block, head
+    order), both with no arithmetic."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_349_amd as pa
+
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nb = w.blocks_per_seq()
+    ids = np.concatenate([w.block_tables[s, :nb[s]] for s in range(w.num_seqs)]).astype(np.int64)
+    tiles_np = (ids[:, None] * w.num_kv_heads + np.arange(w.num_kv_heads)[None, :]).reshape(-1)
+    tiles = torch.from_numpy(tiles_np.astype(np.int32)).to(dev)
+    tile_bytes = w.block_size * w.head_dim * 2
+    tile_total = 2 * tiles.numel() * tile_bytes
+
+    def timed(fn, iters=20):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+    t_pool = timed(lambda: (pa.probe_read(d.k_cache, sink), pa.probe_read(d.v_cache, sink)))
+    pool_bytes = 2 * d.k_cache.numel() * d.k_cache.element_size()
+    t_tiles = timed(lambda: pa.probe_read_tiles(d.k_cache, d.v_cache, tiles, sink))
+    stream_gbps = pool_bytes / (t_pool * 1e-6) / 1e9
+    tiles_gbps = tile_total / (t_tiles * 1e-6) / 1e9
+    kernel_gbps = (w.kv_bytes_unique() + w.small_bytes()) / (kern_mean_us * 1e-6) / 1e9
+    log(f"ceilings: contiguous read {stream_gbps:.0f} GB/s, paged tile read {tiles_gbps:.0f} GB/s")
+    return {
+        "contiguous_read_gbps": round(stream_gbps, 1), "contiguous_read_bytes": pool_bytes,
+        "paged_tile_read_gbps": round(tiles_gbps, 1), "paged_tile_read_bytes": tile_total,
+        "paged_tile_read_us": round(t_tiles, 2),
+        "decode_kernel_vs_paged_tile_read": round(kernel_gbps / tiles_gbps, 4),
+    }
+
+
 def bench_shared_prefix(args, dev, stream):
     """Parallel sampling: 16 prompts of 2048 tokens, 8 samples each with private
     tails of 1..513 tokens (bf16, 32/8 heads, D 128, bs 16).  pa_decode reads
@@ -236,6 +281,8 @@ def parse_args():
                    help="also run one plain 1 GiB device copy (counter calibration)")
     p.add_argument("--no-blocks", action="store_true",
                    help="skip the block-manager, copy-on-write and swap measurements")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the streaming-read and paged-tile-read probes")
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="skip the shared-prefix decode measurement (parallel-sampling workload)")
     p.add_argument("--shared-prefix", action="store_true",
@@ -445,6 +492,9 @@ def main() -> int:
         b.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: one 1 GiB device copy done")
+
+    if not args.no_ceilings:
+        result["ceilings"] = bench_ceilings(w, d, dev, stream, kern_mean)
 
     if not args.no_shared_prefix and args.config == 5:
         result["shared_prefix"] = bench_shared_prefix(args, dev, stream)

@@ -264,6 +264,22 @@ int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
 int pa_kernel_timing_begin(int32_t capacity);
 int pa_kernel_timing_end(double* total_ms, int32_t* launches);
 
+/*
+ * Bandwidth probes, for the benchmark's empirical ceilings (not part of the
+ * decode path).  pa_probe_read reads `bytes` (a multiple of 16) at `src`
+ * once, contiguously.  pa_probe_read_tiles reads, for each listed tile index
+ * t in [0, pool_tiles), the tile_bytes at k_cache + t * tile_bytes and at
+ * v_cache + t * tile_bytes (tile_bytes 4096 or 8192: one (block, KV head)
+ * tile of 16 or 32 tokens x 128 bf16 features); other indices are skipped.
+ * Both use the decode kernel's nontemporal 16-byte loads and do no
+ * arithmetic beyond folding the data into a register; `sink` (one device
+ * word) is written only if that fold equals a fixed 32-bit value.
+ */
+int pa_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int pa_probe_read_tiles(const void* k_cache, const void* v_cache, const int32_t* tiles,
+                        int32_t num_tiles, int32_t tile_bytes, int64_t pool_tiles, uint32_t* sink,
+                        void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(int32_t status);
 

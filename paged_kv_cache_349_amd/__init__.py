@@ -51,6 +51,9 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp] * 8 + [_c_int, ctypes.c_float] + [_c_int] * 8 +
                                 [_vp, ctypes.c_size_t, _c_int, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [_c_int] * 8),
+    "pa_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
+    "pa_probe_read_tiles": (ctypes.c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _vp,
+                                           _vp]),
     "pa_kernel_timing_begin": (ctypes.c_int, [_c_int]),
     "pa_kernel_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(_c_int)]),
@@ -323,6 +326,24 @@ def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, g
         prefix_blocks.data_ptr(), ng, float(scale), bs, S, Hq, Hkv, D, max_blocks, NB, code,
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), partition_tokens, sh))
     return out
+
+
+def probe_read(src, sink, stream=None):
+    """Read all of `src` (a contiguous GPU tensor) once; a bandwidth probe."""
+    dev = _on_gpu(src, sink)
+    _check(load_library().pa_probe_read(src.data_ptr(), src.numel() * src.element_size(),
+                                        sink.data_ptr(), _stream_handle(dev, stream)))
+
+
+def probe_read_tiles(k_cache, v_cache, tiles, sink, stream=None):
+    """Read the K and V tiles listed in `tiles` (int32 tile indices block * Hkv + head)."""
+    dev = _on_gpu(k_cache, v_cache, tiles, sink)
+    NB, Hkv, bs, D = _pool_shape(k_cache, v_cache)
+    tile_bytes = bs * D * k_cache.element_size()
+    _check(load_library().pa_probe_read_tiles(k_cache.data_ptr(), v_cache.data_ptr(),
+                                              tiles.data_ptr(), tiles.numel(), tile_bytes,
+                                              NB * Hkv, sink.data_ptr(),
+                                              _stream_handle(dev, stream)))
 
 
 def kernel_timing_begin(capacity: int):

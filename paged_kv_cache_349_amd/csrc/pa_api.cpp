@@ -440,6 +440,35 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
                       num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, stream);
 }
 
+int pa_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "bytes=%zu and src must be multiples of 16", bytes);
+  hipError_t e = pa::launch_probe_read(src, (int64_t)bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "probe_read launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int pa_probe_read_tiles(const void* k_cache, const void* v_cache, const int32_t* tiles,
+                        int32_t num_tiles, int32_t tile_bytes, int64_t pool_tiles, uint32_t* sink,
+                        void* stream) {
+  if (num_tiles < 0 || pool_tiles < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_tiles=%d pool_tiles=%lld", num_tiles,
+                (long long)pool_tiles);
+  if (tile_bytes != 4096 && tile_bytes != 8192)
+    return fail(PA_ERR_UNSUPPORTED, "tile_bytes=%d is neither 4096 nor 8192", tile_bytes);
+  if (num_tiles == 0) return ok();
+  if (!k_cache || !v_cache || !tiles || !sink) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  hipError_t e = pa::launch_probe_read_tiles(k_cache, v_cache, tiles, num_tiles, tile_bytes,
+                                             pool_tiles, sink, (hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(PA_ERR_LAUNCH, "probe_read_tiles launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int pa_kernel_timing_begin(int32_t capacity) {
   if (capacity <= 0 || capacity > (1 << 20))
     return fail(PA_ERR_INVALID_ARG, "capacity=%d is not in [1, 2^20]", capacity);

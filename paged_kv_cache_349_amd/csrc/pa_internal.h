@@ -101,4 +101,10 @@ hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
 
 bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t group);
 
+// Bandwidth probes (pa_probe.hip).  bytes: a multiple of 16; tile_bytes: 4096 or 8192.
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_read_tiles(const void* k_cache, const void* v_cache, const int32_t* tiles,
+                                   int32_t num_tiles, int32_t tile_bytes, int64_t pool_tiles,
+                                   uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa
