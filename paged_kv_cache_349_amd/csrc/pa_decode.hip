@@ -82,6 +82,32 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum of a value over the four 16-lane rows of a wave (lanes l, l^16,
+// l^32, l^48), with the gfx950 row-swap instructions instead of a shuffle
+// through LDS (which waits for the LDS path twice).  permlane16_swap(x, x)
+// returns the pair {x[l], x[l^16]} in some order in every lane (checked on
+// the device: lane l < 16 gets {x[l], x[l+16]}, lane 16 <= l < 32 gets
+// {x[l-16], x[l]}, likewise for rows 2 and 3); permlane32_swap the same for
+// l^32.  Addition is commutative, so the sums are bitwise those of the
+// shuffles.
+__device__ __forceinline__ float rows_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <typename T>
 __device__ __forceinline__ float widen(T x);
 template <>
@@ -634,8 +660,7 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
             sc[sb][rr] = x;
             mx = fmaxf(mx, x);
           }
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        mx = rows_max(mx);
         const float mnew = fmaxf(m[hh], mx);
         const float mref = mnew == kNegInf ? 0.f : mnew;
         const float alpha = exp2_fast(m[hh] - mref);
@@ -685,8 +710,7 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float ls = lsum[hh];
-      ls += shfl_xor_f(ls, 16);
-      ls += shfl_xor_f(ls, 32);
+      ls = rows_sum(ls);
       const int r = hh * 16 + col;
       if (quad == 0) {
         sm_m[w * kPrefixRows + r] = m[hh];
@@ -884,8 +908,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         sc[sb][rr] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = rows_max(mx);
     const float mnew = fmaxf(m, mx);
     // Exponent reference: the running max, or 0 while every position seen so
     // far is masked (then all weights, the rescale factor included, are 0).
@@ -903,12 +926,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         psum += bf16_bits_to_f32(bits);
       }
     lsum = lsum * alpha + psum;
-    // alpha is exactly 1 for every head whose running max did not move, which
-    // after the first blocks is nearly always: skip the rescale then.
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    // Rescale every time (alpha is exactly 1 while a head's running max holds,
+    // and multiplying by 1 changes nothing): skipping it behind a wave-uniform
+    // test made the compiler copy the 32 accumulator registers at every
+    // position, which cost as much as the multiplies.
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
-    }
+    for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
     // Partly dead block: zero V of dead positions (their weight is 0, but
     // 0 * NaN is NaN).
     if (live < 16) {
@@ -954,8 +977,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
       __builtin_amdgcn_s_sleep(1);
     }
     float ls = lsum;
-    ls += shfl_xor_f(ls, 16);
-    ls += shfl_xor_f(ls, 32);
+    ls = rows_sum(ls);
     // State index = the wave's lane in the item, so the merge below adds the
     // partial states in an order fixed by logical positions.
     if (quad == 0) {
