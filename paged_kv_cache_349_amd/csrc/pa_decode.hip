@@ -7,29 +7,32 @@
 //
 // Work items.  A sequence's context is cut into partitions of part_blocks
 // logical blocks; one work item is (sequence s, KV head h, partition p).
-// The cut depends only on the sequence's own length, so every reduction
-// order below depends only on logical positions: results are bitwise
-// reproducible, independent of where blocks sit in the pool and of the
-// other sequences in the batch.
+// The partition size is chosen per call from the batch's lengths (or given
+// by the caller); for a given batch every reduction order depends only on
+// logical positions, so results are bitwise reproducible and independent of
+// where blocks sit in the pool.
 //
-// Two launches on the caller's stream:
-//   plan_items    one workgroup.  Lists the non-empty (s, p) pairs in the
-//                 workspace -- every full partition first (sequence order),
-//                 then the partial last partitions in decreasing size -- and
-//                 clears the merge counters.
+// Three launches on the caller's stream:
+//   plan_items    one workgroup (sharing its launch with the slot write when
+//                 a whole step is issued).  Picks the partition size and
+//                 lists the non-empty (s, p) pairs in the workspace -- every
+//                 full partition first (sequence order), then the partial
+//                 last partitions in decreasing size -- plus the sequences
+//                 whose partition states must be merged, and, with shared
+//                 prefixes, each group's shared blocks and the prefix items.
 //   decode_*      persistent: as many workgroups as fit on the chip at once,
 //                 dealt the list in snake order, so no workgroup is launched
 //                 for an empty partition and the work per workgroup stays
 //                 even however ragged the context lengths are.
+//   merge_splits  log-sum-exp merge, in partition order, of the partition
+//                 states of every sequence listed by the planner.
 //
 // Inside an item, the wave in lane j of the W lanes takes logical blocks
 // b0 + j, b0 + j + W, ... and keeps a running softmax state (max m, sum l,
 // weighted sum acc) per query head of the group; the W states are merged
 // through LDS in lane order.  A sequence with one partition writes `out`
-// directly.  Otherwise the item stores its partition state in the workspace
-// and bumps the (s, h) arrival counter; the workgroup that brings it to the
-// partition count merges all partitions of (s, h) with a log-sum-exp
-// combination, in partition order, and writes `out`.
+// directly; otherwise the item stores its partition state in the workspace
+// for merge_splits.
 //
 // Matrix-core kernel (bf16).  For each 16-token sub-block:
 //   S^T[16 tokens x 16 heads] = K[16 x D] * Q^T[D x 16]      (v_mfma_f32_16x16x32_bf16)
@@ -46,6 +49,10 @@
 //
 // Vector-ALU kernel (fp32, and bf16 on request): the same items and merge;
 // scores by lanes over tokens, weighted values by lanes over features.
+//
+// Shared prefixes (pa_decode_shared_prefix): the matrix-core kernel first
+// runs prefix items that read each shared block once for up to 32 query
+// rows (see prefix_items), then the sequences' own blocks as above.
 #include <hip/hip_runtime.h>
 
 #include <map>
