@@ -19,8 +19,14 @@
  *                   gathering the KV into one buffer.
  *
  * Layout (all row-major; the same on every entry point):
- *   k_cache  [num_blocks, num_kv_heads, block_size, head_dim]   kv dtype
- *   v_cache  [num_blocks, num_kv_heads, head_dim, block_size]   kv dtype
+ *   k_cache  [num_blocks, num_kv_heads, block_size, head_dim]       kv dtype
+ *   v_cache  [num_blocks, num_kv_heads, (block_size/T)*head_dim, T]  kv dtype
+ *   T = 16 when 16 divides block_size, otherwise T = block_size: V is kept
+ *   feature-major in sub-tiles of T tokens, so token o's feature d is
+ *   v_cache[b, h, (o/T)*head_dim + d, o%T].  For block_size <= 16 this is
+ *   plainly [num_blocks, num_kv_heads, head_dim, block_size].  Every 16-token
+ *   piece of a (block, KV head) tile is then one contiguous span of K and one
+ *   of V.
  *   A slot is physical_block * block_size + offset_in_block.
  *   Query head h reads KV head h / (num_heads / num_kv_heads).
  *   out = softmax(scale * q . K^T) . V over positions 0 .. context_len-1.
@@ -71,7 +77,8 @@ typedef enum pa_status {
 /*
  * Slot write.  For t in [0, num_tokens): if slot_mapping[t] >= 0, with
  * b = slot / block_size and o = slot % block_size,
- *   k_cache[b, h, o, :] = k_new[t, h, :]   and   v_cache[b, h, :, o] = v_new[t, h, :]
+ *   k_cache[b, h, o, :] = k_new[t, h, :]   and
+ *   v_cache[b, h, (o/T)*head_dim + d, o%T] = v_new[t, h, d]  for every d
  * for every KV head h.  The copy moves raw element bits (NaN payloads
  * included).  A negative slot is skipped.  Slots must be distinct.
  *

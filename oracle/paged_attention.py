@@ -20,7 +20,11 @@ path computes, written from the pages:
 
 Readings where the pages are silent (shared with the HIP side only as a
 written convention, never as code):
-  * k_cache [NB, Hkv, bs, D], v_cache [NB, Hkv, D, bs]; slot = block*bs + offset.
+  * k_cache [NB, Hkv, bs, D]; slot = block*bs + offset.  v_cache is
+    feature-major in sub-tiles of T tokens (T = 16 when 16 divides bs, else
+    T = bs): v_cache [NB, Hkv, (bs/T)*D, T], and token o's feature d sits at
+    [block, head, (o // T)*D + d, o % T].  With bs <= 16 that is plainly
+    [NB, Hkv, D, bs].
   * Scores are scale * q.k over positions 0 .. L-1 (one query at the last
     position, so no causal mask is needed); no bias of any kind.
   * Query head h reads KV head h // (Hq // Hkv).
@@ -59,6 +63,20 @@ def _raw_view(x: np.ndarray) -> np.ndarray:
     raise TypeError(x.dtype)
 
 
+def v_tile_tokens(block_size):
+    """Tokens per feature-major V sub-tile (a layout convention, see above)."""
+    return 16 if block_size % 16 == 0 else block_size
+
+
+def _v_tiles(v_cache, block_size):
+    """The V pool as [NB, Hkv, bs/T, D, T] (a view: only the axes are split)."""
+    T = v_tile_tokens(block_size)
+    NB, Hkv, R, cols = v_cache.shape
+    if cols != T or R % (block_size // T):
+        raise ValueError(f"v_cache shape {v_cache.shape} does not fit block_size {block_size}")
+    return v_cache.reshape(NB, Hkv, block_size // T, R // (block_size // T), T)
+
+
 def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
     """Slot write: new token t's K/V go to slot_mapping[t] of the pool.
 
@@ -68,15 +86,16 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
     """
     k_out = k_cache.copy()
     v_out = v_cache.copy()
-    kr, vr = _raw_view(k_out), _raw_view(v_out)
+    kr, vr = _raw_view(k_out), _v_tiles(_raw_view(v_out), block_size)
     knr, vnr = _raw_view(np.ascontiguousarray(k_new)), _raw_view(np.ascontiguousarray(v_new))
+    T = v_tile_tokens(block_size)
     for t in range(len(slot_mapping)):
         slot = int(slot_mapping[t])
         if slot < 0:
             continue
         b, o = divmod(slot, block_size)
-        kr[b, :, o, :] = knr[t]          # K tile keeps a token's features together
-        vr[b, :, :, o] = vnr[t]          # V tile keeps a feature's tokens together
+        kr[b, :, o, :] = knr[t]              # K tile keeps a token's features together
+        vr[b, :, o // T, :, o % T] = vnr[t]  # V sub-tile keeps a feature's tokens together
     return k_out, v_out
 
 
@@ -89,8 +108,9 @@ def gather_sequence(k_cache, v_cache, table_row, L, block_size, kv_dtype):
     pos = np.arange(L)
     blocks = np.asarray(table_row)[pos // block_size].astype(np.int64)
     offs = pos % block_size
-    K = k_cache[blocks, :, offs, :]          # [L, Hkv, D]
-    V = v_cache[blocks, :, :, offs]          # [L, Hkv, D]
+    T = v_tile_tokens(block_size)
+    K = k_cache[blocks, :, offs, :]                                  # [L, Hkv, D]
+    V = _v_tiles(v_cache, block_size)[blocks, :, offs // T, :, offs % T]  # [L, Hkv, D]
     K = widen(K, kv_dtype).transpose(1, 0, 2)
     V = widen(V, kv_dtype).transpose(1, 0, 2)
     return K, V

@@ -10,8 +10,10 @@ raises.
     copy_blocks(k_cache, v_cache, src_blocks, dst_blocks)           # copy-on-write
     swap_blocks(dst_k, dst_v, src_k, src_v, src_blocks, dst_blocks)   # device <-> pinned host
 
-Layouts: k_cache [NB, Hkv, bs, D], v_cache [NB, Hkv, D, bs] (float32 or
-bfloat16); q [S, Hq, D] and k_new/v_new [T, Hkv, D] in the cache dtype;
+Layouts: k_cache [NB, Hkv, bs, D] and v_cache [NB, Hkv, (bs/T)*D, T] with
+T = 16 when 16 divides bs, else T = bs (V feature-major in T-token sub-tiles;
+[NB, Hkv, D, bs] for bs <= 16), float32 or bfloat16 (`v_pool_shape`);
+q [S, Hq, D] and k_new/v_new [T, Hkv, D] in the cache dtype;
 out [S, Hq, D] float32; block_tables [S, max_blocks] int32; context_lens [S]
 int32; slot_mapping [T] int32.
 """
@@ -126,6 +128,15 @@ def _on_gpu(*ts):
     return dev
 
 
+def v_pool_shape(num_blocks, num_kv_heads, head_dim, block_size):
+    """Shape of the V pool for a K pool [num_blocks, num_kv_heads, block_size, head_dim]."""
+    T = 16 if block_size % 16 == 0 else block_size
+    return (num_blocks, num_kv_heads, (block_size // T) * head_dim, T)
+
+
+_V_SHAPE_MSG = "v_cache must be [NB, Hkv, (bs/T)*D, T], T = 16 if 16 divides bs else bs"
+
+
 def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     """Copy new tokens' K/V into their slots (raw bits; slot < 0 skipped)."""
     torch = _torch()
@@ -133,7 +144,7 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     dev = _on_gpu(k_cache, v_cache, k_new, v_new, slot_mapping)
     _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-D")
     NB, Hkv, bs, D = k_cache.shape
-    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(tuple(v_cache.shape) == v_pool_shape(NB, Hkv, D, bs), _V_SHAPE_MSG)
     _need(k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype, "dtype mismatch")
     _need(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1, "slot_mapping: int32 [T]")
     T = slot_mapping.shape[0]
@@ -147,7 +158,7 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
 def _pool_shape(k, v):
     _need(k.dim() == 4 and v.dim() == 4, "caches must be 4-D")
     NB, Hkv, bs, D = k.shape
-    _need(tuple(v.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(tuple(v.shape) == v_pool_shape(NB, Hkv, D, bs), _V_SHAPE_MSG)
     _need(k.dtype == v.dtype, "k and v caches must share a dtype")
     return NB, Hkv, bs, D
 
@@ -228,7 +239,7 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens)
     NB, Hkv, bs, D = k_cache.shape
     _need(bs == block_size, f"block_size={block_size} but k_cache has {bs}")
-    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(tuple(v_cache.shape) == v_pool_shape(NB, Hkv, D, bs), _V_SHAPE_MSG)
     _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
     S, Hq, _ = q.shape
     _need(q.dtype == k_cache.dtype == v_cache.dtype, "q and caches must share a dtype")
@@ -359,5 +370,5 @@ def kernel_timing_end():
     return ms.value, n.value
 
 
-__all__ = ["write_kv", "decode", "decode_step", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+__all__ = ["v_pool_shape", "write_kv", "decode", "decode_step", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
            "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]

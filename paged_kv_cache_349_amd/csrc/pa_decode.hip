@@ -507,20 +507,19 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane, int group) {
   const uint32_t row = lane & 15, quad = lane >> 4;
   LaneOff o;
   o.k = (row * D + quad * 8) * 2;      // K row `row`, features 8*quad ..
-  o.v = (row * BS + quad * 4) * 2;     // V feature `row`, tokens 4*quad ..
+  o.v = (row * 16 + quad * 4) * 2;     // V feature `row`, tokens 4*quad .. of a 16-token sub-tile
   // Query head `row` of the group; padding heads point past the group so
   // their loads return zeros.
   o.q = (int)row < group ? (row * D + quad * 8) * 2 : (uint32_t)group * D * 2;
   return o;
 }
 
-// One 16-token half of a K/V tile of BS tokens (half < BS / 16).  With
-// BS = 32 a V half covers half of every 64-byte feature row, and the other
-// half of those lines is read by the next position: V then keeps the default
-// cache policy, so that read finds the lines in the cache (measured on the
-// large-batch workload at block size 32: 254.6 us per call against 290.0 us
-// with nontemporal V loads; 265 us for whole 32-token tiles, which need twice
-// the registers and so half the occupancy).
+// One 16-token half of a K/V tile of BS tokens (half < BS / 16).  The K
+// rows of the half and its feature-major V sub-tile ([D, 16]) are each one
+// contiguous 16*D-element span, so a half reads whole cache lines whatever BS
+// is (measured on the large-batch workload at block size 32: 208.8 us per
+// call with V in 16-token sub-tiles, against 240.3 us with V feature-major
+// over the whole 32-token block, where a half covers half of every line).
 template <int D, int BS>
 __device__ __forceinline__ void load_half(Tile<D, 16>& t, __amdgpu_buffer_rsrc_t kr,
                                           __amdgpu_buffer_rsrc_t vr, const LaneOff& o, int half) {
@@ -532,8 +531,8 @@ __device__ __forceinline__ void load_half(Tile<D, 16>& t, __amdgpu_buffer_rsrc_t
 #pragma unroll
   for (int i = 0; i < D / 16; ++i)
     t.v[0][i] = __builtin_bit_cast(
-        i16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, o.v + (i * 16 * BS + half * 16) * 2, 0,
-                                                    BS == 16 ? kStreamLoad : 0));
+        i16x4, __builtin_amdgcn_raw_buffer_load_b64(vr, o.v + (half * 16 * D + i * 16 * 16) * 2,
+                                                    0, kStreamLoad));
 }
 
 // Read-only views through the constant address space: uniform reads of
@@ -1122,6 +1121,7 @@ __device__ __forceinline__ void valu_item(const DecodeParams& a, const Item& it,
   constexpr int NC = 64 / BS;          // lanes per token in the score step
   constexpr int DC = D / NC;           // features per lane in the score step
   constexpr int DL = D / 64;           // features per lane in the weighted sum
+  constexpr int VT = BS % 16 == 0 ? 16 : BS;  // tokens per feature-major V sub-tile
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.group;
@@ -1189,7 +1189,7 @@ __device__ __forceinline__ void valu_item(const DecodeParams& a, const Item& it,
     for (int t = 0; t < valid; ++t) {
 #pragma unroll
       for (int k = 0; k < DL; ++k) {
-        const float vv = widen<T>(vt[(lane + 64 * k) * BS + t]);
+        const float vv = widen<T>(vt[((t / VT) * D + lane + 64 * k) * VT + t % VT]);
 #pragma unroll
         for (int g = 0; g < kMaxGroup; ++g)
           if (g < G) acc[g][k] += p_w[g * BS + t] * vv;

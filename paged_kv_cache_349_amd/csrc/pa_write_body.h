@@ -19,14 +19,17 @@ struct WriteArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
+  int32_t v_tile;       // tokens per feature-major V sub-tile: 16 if 16 | block_size, else block_size
   int64_t num_slots;    // num_blocks * block_size
   int32_t elem_bytes;   // 2 (bf16) or 4 (fp32)
 };
 
 // Elements first, first + stride, ... of the write: one per (token, kv head,
 // feature).  Reads of k_new/v_new and the K-cache writes are contiguous along
-// the feature; V-cache writes stride by block_size elements because a V tile
-// keeps each feature's tokens together.  Raw bits are copied (uint16 / uint32).
+// the feature; V-cache writes stride by v_tile elements because a V sub-tile
+// keeps each feature's tokens together (token o, feature d of a tile at
+// ((o / v_tile) * head_dim + d) * v_tile + o % v_tile).  Raw bits are copied
+// (uint16 / uint32).
 template <typename E>
 __device__ __forceinline__ void write_elements(const WriteArgs& w, int64_t first, int64_t stride) {
   E* __restrict__ kc = (E*)w.k_cache;
@@ -43,8 +46,10 @@ __device__ __forceinline__ void write_elements(const WriteArgs& w, int64_t first
     const int64_t b = slot / w.block_size;
     const int32_t o = (int32_t)(slot % w.block_size);
     const int64_t tile = b * w.num_kv_heads + h;
+    const int32_t sub = o / w.v_tile;
     kc[(tile * w.block_size + o) * w.head_dim + d] = kn[i];
-    vc[(tile * w.head_dim + d) * w.block_size + o] = vn[i];
+    vc[tile * w.block_size * w.head_dim + ((int64_t)sub * w.head_dim + d) * w.v_tile +
+       (o - sub * w.v_tile)] = vn[i];
   }
 }
 

@@ -40,6 +40,7 @@ WriteArgs make_write_args(void* k_cache, void* v_cache, const void* k_new, const
   w.num_kv_heads = num_kv_heads;
   w.head_dim = head_dim;
   w.block_size = block_size;
+  w.v_tile = block_size % 16 == 0 ? 16 : block_size;
   w.num_slots = (int64_t)num_blocks * block_size;
   w.elem_bytes = type == KvType::BF16 ? 2 : 4;
   return w;

@@ -19,10 +19,12 @@ sit at unrelated physical addresses, as in the block-mapping diagram of
 
 Cache layout (a boundary decision, the same on both sides of every test):
   k_cache [num_blocks, num_kv_heads, block_size, head_dim]
-  v_cache [num_blocks, num_kv_heads, head_dim, block_size]
+  v_cache [num_blocks, num_kv_heads, (block_size / T) * head_dim, T]
+with T = 16 when 16 divides block_size, else T = block_size (`v_pool_shape`).
 For one (block, kv head) both tiles are contiguous spans of
 block_size * head_dim elements.  K keeps a token's head_dim values together;
-V keeps a feature's block_size token values together.
+V keeps a feature's T token values together, in sub-tiles of T tokens
+(token o, feature d at row (o // T) * head_dim + d, column o % T).
 
 Element storage: fp32 values are held as np.float32; bf16 values are held as
 their raw 16-bit patterns in np.uint16 (NumPy has no bf16 type).  fp32 draws
@@ -96,7 +98,7 @@ class Workload:
     context_lens: np.ndarray   # int32 [S]
     block_tables: np.ndarray   # int32 [S, max_blocks], padding -1
     k_cache: np.ndarray        # [NB, Hkv, bs, D]
-    v_cache: np.ndarray        # [NB, Hkv, D, bs]
+    v_cache: np.ndarray        # v_pool_shape(NB, Hkv, D, bs)
     q: np.ndarray              # [S, Hq, D]
     k_new: np.ndarray          # [S, Hkv, D]
     v_new: np.ndarray          # [S, Hkv, D]
@@ -194,6 +196,12 @@ def new_token_slot(table_row: np.ndarray, L: int, block_size: int) -> int:
     return int(table_row[pos // block_size]) * block_size + pos % block_size
 
 
+def v_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int):
+    """Shape of the V pool: feature-major sub-tiles of T tokens (layout above)."""
+    T = 16 if block_size % 16 == 0 else block_size
+    return (num_blocks, num_kv_heads, (block_size // T) * head_dim, T)
+
+
 def _poison_fill(rng: np.random.Generator, k_cache, v_cache, live_mask, kv_dtype, poison):
     """Overwrite every (block, offset) slot that is not live with poison.
 
@@ -211,9 +219,12 @@ def _poison_fill(rng: np.random.Generator, k_cache, v_cache, live_mask, kv_dtype
     kview = k_cache if kv_dtype == BF16 else k_cache.view(np.uint32)
     vview = v_cache if kv_dtype == BF16 else v_cache.view(np.uint32)
     pick = nans[np.arange(dead_b.size) % nans.size]
-    # K: [NB, Hkv, bs, D] -> slot (b, :, o, :);  V: [NB, Hkv, D, bs] -> (b, :, :, o)
+    # K: [NB, Hkv, bs, D] -> slot (b, :, o, :);  V sub-tiles -> (b, :, o // T, :, o % T)
+    NB, Hkv, R, T = vview.shape
+    bs = kview.shape[2]
+    vtiles = vview.reshape(NB, Hkv, bs // T, R // (bs // T), T)
     kview[dead_b, :, dead_o, :] = pick[:, None, None]
-    vview[dead_b, :, :, dead_o] = pick[:, None, None]
+    vtiles[dead_b, :, dead_o // T, :, dead_o % T] = pick[:, None, None]
 
 
 def build_workload(name: str, rng: np.random.Generator, *, kv_dtype: str, context_lens,
@@ -267,7 +278,7 @@ def build_workload(name: str, rng: np.random.Generator, *, kv_dtype: str, contex
 
     Hkv, D = num_kv_heads, head_dim
     k_cache = _draw(rng, (num_blocks, Hkv, bs, D), kv_dtype)
-    v_cache = _draw(rng, (num_blocks, Hkv, D, bs), kv_dtype)
+    v_cache = _draw(rng, v_pool_shape(num_blocks, Hkv, D, bs), kv_dtype)
     q = _draw(rng, (S, num_heads, D), kv_dtype)
     k_new = _draw(rng, (S, Hkv, D), kv_dtype)
     v_new = _draw(rng, (S, Hkv, D), kv_dtype)
@@ -452,12 +463,14 @@ def pack_logical(logical_k: List[np.ndarray], logical_v: List[np.ndarray], table
     Hkv, _, D = logical_k[0].shape
     dt = logical_k[0].dtype
     k = np.full((num_blocks, Hkv, block_size, D), fill, dtype=dt)
-    v = np.full((num_blocks, Hkv, D, block_size), fill, dtype=dt)
+    v = np.full(v_pool_shape(num_blocks, Hkv, D, block_size), fill, dtype=dt)
+    T = v.shape[3]
     for s, (ks, vs) in enumerate(zip(logical_k, logical_v)):
         L = ks.shape[1]
         for p in range(L):
             b = int(tables[s, p // block_size])
             o = p % block_size
             k[b, :, o, :] = ks[:, p, :]
-            v[b, :, :, o] = vs[:, p, :]
+            row = (o // T) * D
+            v[b, :, row:row + D, o % T] = vs[:, p, :]
     return k, v

@@ -38,7 +38,7 @@ def _raw(a):
 
 def _pool(rng, NB, Hkv, bs, D, dt, nan_share=0.0):
     k = wl._draw(rng, (NB, Hkv, bs, D), dt)
-    v = wl._draw(rng, (NB, Hkv, D, bs), dt)
+    v = wl._draw(rng, wl.v_pool_shape(NB, Hkv, D, bs), dt)
     if nan_share:
         nan = np.uint16(0x7FC1) if dt == "bf16" else np.float32("nan")
         k.reshape(-1)[rng.random(k.size) < nan_share] = nan
@@ -165,9 +165,9 @@ def test_serving_loop_with_sharing_cow_and_swap(dt):
     nan = np.uint16(0x7FC1) if dt == "bf16" else np.float32("nan")
     st = np.uint16 if dt == "bf16" else np.float32
     k = np.full((NB, Hkv, bs, D), nan, st)
-    v = np.full((NB, Hkv, D, bs), nan, st)
+    v = np.full(wl.v_pool_shape(NB, Hkv, D, bs), nan, st)
     hk = np.full((NH, Hkv, bs, D), nan, st)
-    hv = np.full((NH, Hkv, D, bs), nan, st)
+    hv = np.full(wl.v_pool_shape(NH, Hkv, D, bs), nan, st)
     kd, vd = _dev(k, dt), _dev(v, dt)
     hkd, hvd = _dev(hk, dt, pinned=True), _dev(hv, dt, pinned=True)
     m = BlockManager(NB, NH, bs, MB, device_free_order=rng.permutation(NB))

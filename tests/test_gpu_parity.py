@@ -220,6 +220,24 @@ def test_bit_exact_write_of_nan_payloads():
         assert np.array_equal(_raw(torch_to_np(d.v_cache, dt)), _raw(v_ref))
 
 
+@pytest.mark.parametrize("bs", [1, 7, 24, 48, 64])
+def test_write_other_block_sizes(bs):
+    """The slot write at block sizes the decode kernels are not compiled for:
+    V whole-block feature-major (1, 7, 24) or in 16-token sub-tiles (48, 64)."""
+    import paged_kv_cache_349_amd as pa
+    import torch
+    from paged_kv_cache_349_amd.device_io import torch_to_np, upload
+    for dt in ("f32", "bf16"):
+        _say(f"write bs={bs} {dt}")
+        w = _custom([1, bs, 3 * bs + 2, 100], 8, 2, 64, bs, dt, seed=bs)
+        k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, bs)
+        d = upload(w)
+        pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+        torch.cuda.synchronize()
+        assert np.array_equal(_raw(torch_to_np(d.k_cache, dt)), _raw(k_ref))
+        assert np.array_equal(_raw(torch_to_np(d.v_cache, dt)), _raw(v_ref))
+
+
 def test_kernel_timing_events():
     """Kernel timing records one event pair per decode call, up to its capacity."""
     import paged_kv_cache_349_amd as pa

@@ -65,14 +65,17 @@ def pin_library_routine(decode, seed=0):
     """P1 + P8: paged oracle == torch SDPA (fp64) on the logical tensors.
 
     Covers MHA (G=1) and GQA (G=4) with the KV heads expanded per query head,
-    shuffled tables, block sizes 1, 4 and 16 and ragged lengths.
+    shuffled tables, block sizes 1, 4, 16, 32 and 48 (V in 16-token sub-tiles
+    for the last two) and ragged lengths.
     """
     rng = np.random.default_rng(seed)
     worst = 0.0
     for (Hq, Hkv, D, bs, lens) in [(4, 4, 16, 16, [1, 17, 40, 5]),
                                    (8, 2, 8, 4, [3, 9, 30]),
                                    (6, 3, 4, 1, [7, 2]),
-                                   (4, 1, 32, 16, [64, 33])]:
+                                   (4, 1, 32, 16, [64, 33]),
+                                   (4, 2, 8, 32, [70, 33, 1]),
+                                   (2, 1, 4, 48, [100, 47])]:
         lk, lv, q, kc, vc, tables, L = _random_paged(rng, lens, Hq, Hkv, D, bs)
         sc = np.float32(1.0 / math.sqrt(D))
         out = decode(q, kc, vc, tables, L, sc, bs, "f32")
@@ -93,7 +96,7 @@ def pin_brute_force(decode, cases=20, seed=1):
     rng = np.random.default_rng(seed)
     worst = 0.0
     for c in range(cases):
-        bs = [1, 2, 4, 16][c % 4]
+        bs = [1, 2, 4, 16, 32][c % 5]
         Hkv = 1 + c % 2
         G = 1 + (c // 2) % 3
         D = 1 + int(rng.integers(1, 8))
@@ -347,11 +350,18 @@ def _mutant_decode(kind):
                 bl = block_tables[s][pos % max(1, (L + block_size - 1) // block_size)].astype(np.int64)
             off = pos % block_size
             K = oracle.widen(k_cache[bl, :, off, :], kv_dtype).transpose(1, 0, 2)
-            if kind == "v_as_k_layout":
+            if kind == "v_whole_block_tile":             # V feature-major over the whole block
+                whole = v_cache.reshape(v_cache.shape[0], Hkv, D, block_size)
+                V = oracle.widen(whole[bl, :, :, off], kv_dtype)
+                V = V.transpose(1, 0, 2)
+            elif kind == "v_as_k_layout":
                 V = oracle.widen(v_cache.reshape(k_cache.shape)[bl, :, off, :], kv_dtype)
                 V = V.transpose(1, 0, 2)
             else:
-                V = oracle.widen(v_cache[bl, :, :, off], kv_dtype).transpose(1, 0, 2)
+                T = v_cache.shape[3]           # feature-major sub-tiles of T tokens
+                rows = (off // T)[:, None] * D + np.arange(D)[None, :]
+                V = oracle.widen(v_cache[bl[:, None], :, rows, (off % T)[:, None]], kv_dtype)
+                V = V.transpose(2, 0, 1)
             for h in range(Hq):
                 kv = (h % Hkv) if kind == "gqa_modulo" else h // G
                 x = (1.0 if kind == "no_scale" else sc) * (K[kv] @ qd[s, h])
@@ -380,6 +390,7 @@ def _fails_some_pin(dec):
 
 
 @pytest.mark.parametrize("kind", ["drop_last_token", "offset_from_block", "v_as_k_layout",
+                                  "v_whole_block_tile",
                                   "gqa_modulo", "no_scale", "neg_scores", "no_normalise"])
 def test_planted_mistake_is_caught(kind):
     assert _fails_some_pin(_mutant_decode(kind)), kind
