@@ -183,6 +183,51 @@ def bench_shared_prefix(args, dev, stream):
     }
 
 
+def bench_block_size_32(args, dev, stream):
+    """The large-batch workload's block-size-32 variant (same lengths, own pool):
+    whole steps through pa_decode_step timed back to back, then the attention
+    kernel alone by the library's events."""
+    import torch
+
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd import workloads as wl
+    from paged_kv_cache_349_amd.device_io import upload
+
+    w = wl.make_config(5, block_size=32, seed=args.seed)
+    d = upload(w, dev)
+
+    def step():
+        pa.decode_step(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping, d.out, d.q,
+                       d.block_tables, d.context_lens, float(w.scale), w.block_size)
+
+    K = max(20, min(args.steps, 100))
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / K
+    pa.kernel_timing_begin(K)
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    kern_ms, kern_n = pa.kernel_timing_end()
+    kern_us = kern_ms * 1e3 / kern_n
+    alg = w.kv_bytes_unique() + w.small_bytes()
+    log(f"block size 32: {us:.1f} us/step, attention kernel {kern_us:.1f} us")
+    del d
+    return {
+        "workload": w.name, "block_size": 32, "num_blocks": w.num_blocks, "steps": K,
+        "us_per_step": round(us, 2),
+        "kv_gbps_step": round(w.kv_bytes_logical() / (us * 1e-6) / 1e9, 2),
+        "kernel_us_mean": round(kern_us, 2),
+        "kernel_frac": round(alg / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_launch": alg,
+    }
+
+
 PCIE_GEN5_X16_GBPS = 63.0   # 32 GT/s x 16 lanes, 128b/130b coding, per direction
 
 
@@ -283,6 +328,8 @@ def parse_args():
                    help="skip the block-manager, copy-on-write and swap measurements")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the streaming-read and paged-tile-read probes")
+    p.add_argument("--no-bs32", action="store_true",
+                   help="skip the block-size-32 variant of the large-batch workload")
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="skip the shared-prefix decode measurement (parallel-sampling workload)")
     p.add_argument("--shared-prefix", action="store_true",
@@ -495,6 +542,10 @@ def main() -> int:
 
     if not args.no_ceilings:
         result["ceilings"] = bench_ceilings(w, d, dev, stream, kern_mean)
+
+    if not args.no_bs32 and args.config == 5 and args.block_size == 16 \
+            and not args.shared_prefix:
+        result["block_size_32"] = bench_block_size_32(args, dev, stream)
 
     if not args.no_shared_prefix and args.config == 5:
         result["shared_prefix"] = bench_shared_prefix(args, dev, stream)

@@ -42,8 +42,10 @@
 // holds scores of tokens 4*(l/16)+r (r < 4) for head l%16, which is exactly
 // the B operand layout the PV product needs, so P never leaves registers.
 // K rows are loaded straight into the A operand (16 bytes per lane per
-// instruction); V is stored transposed per block (feature-major), so each lane
-// loads 4 consecutive tokens of one feature (8 bytes) for the PV A operand.
+// instruction); V is stored feature-major in 16-token sub-tiles ([D, 16] per
+// 16 tokens of a block), so each lane loads 4 consecutive tokens of one
+// feature (8 bytes) for the PV A operand and every 16-token position reads
+// one contiguous 4 KB span of K and one of V (D = 128, bf16).
 // P is rounded to bf16 for the PV product; the softmax denominator sums those
 // same rounded weights, so the output is an exact convex combination of them.
 //
