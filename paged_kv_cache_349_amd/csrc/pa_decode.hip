@@ -21,9 +21,11 @@
 //                 whose partition states must be merged, and, with shared
 //                 prefixes, each group's shared blocks and the prefix items.
 //   decode_*      persistent: as many workgroups as fit on the chip at once,
-//                 dealt the list in snake order, so no workgroup is launched
-//                 for an empty partition and the work per workgroup stays
-//                 even however ragged the context lengths are.
+//                 dealt the first round of the list and claiming the rest
+//                 from per-pool counters (the vector-ALU kernel deals every
+//                 round in snake order), so no workgroup is launched for an
+//                 empty partition and the workgroups end close together
+//                 however ragged the context lengths are.
 //   merge_splits  log-sum-exp merge, in partition order, of the partition
 //                 states of every sequence listed by the planner.
 //
@@ -233,6 +235,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     a.ws_ctrl[kCtrlPrefixPart] = pbp;
     a.ws_ctrl[kCtrlAbort] = 0;
   }
+  if (tid < kClaimPools) a.ws_ctrl[kCtrlClaims + tid * kClaimStride] = 0;
 
   // Partial last partition of a sequence's own blocks: size class, larger
   // partitions in lower classes.  -1 if there is no partial partition.
@@ -769,7 +772,7 @@ struct Desc {
 };
 
 // Persistent matrix-core kernel.  Each wave walks one stream of positions:
-// item after item (snake order, as for run_items), one position per block it
+// item after item (dealt, then claimed; see item_for), one position per block it
 // owns in the item, and one empty position in an item where it owns none.
 // Every step issues the loads of the next position -- which may belong to
 // the next item -- into one register buffer and computes the current
@@ -809,18 +812,64 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
                                       __HIP_MEMORY_SCOPE_AGENT);
   };
 
-  // The workgroup's item for round r: the list (longest items first) is
-  // dealt to the NG resident workgroups in snake order -- round r gives item
-  // r*NG + b to workgroup b when r is even and to workgroup NG-1-b when r is
-  // odd -- which evens out the work per workgroup without a shared counter.
-  // (A shared counter handing out items on demand was measured slower: the
-  // two workgroups sharing a CU stream at different speeds, and the slower
-  // one then holds long items to the end.)
+  // The workgroup's item for round r.  The list (longest items first) is
+  // dealt, in snake order, for the first round only -- item b to workgroup
+  // b -- and claimed after that: workgroup b takes the next unclaimed item of
+  // pool x = b % kClaimPools (items NG + x, NG + x + kClaimPools, ...) until
+  // the pool is empty.  The two workgroups sharing a CU stream at different
+  // speeds (the first dispatched one gets most of the memory pipeline), and
+  // so do CUs on more or less loaded memory paths; claiming lets the faster
+  // ones take more of the list, so the workgroups end closer together.
+  // Measured on the large-batch workload (512 workgroups, ~4.5 items each):
+  // 209.3 us per call with every round dealt in snake order, 204.4 us with 8
+  // pools, 199.7 us with 32 (contention on each counter falls), 200.5 us with
+  // 64, 202.3 us with 128 (a pool's items are shared by fewer workgroups);
+  // claiming the first round too, 201.5 us.  The first wave to need round
+  // r's item claims it (one device-scope atomic) and publishes it in LDS for
+  // the other waves.  Who computes an item never changes its result.  With
+  // fewer than two rounds of items every round is dealt in snake order
+  // (round r gives item r*NG + b to workgroup b when r is even and to
+  // workgroup NG-1-b when r is odd).
   auto item_of = [&](int r) -> int { return r * NG + ((r & 1) ? NG - 1 - bid : bid); };
+  const bool claimed_rounds = total >= 2 * NG;
+  __shared__ int s_claim_busy[4];   // last round whose claim was started
+  __shared__ int s_claim_tag[4];    // last round whose claim is published
+  __shared__ int s_claim_item[4];
+  auto item_for = [&](int r) -> int {
+    if (r == 0 || !claimed_rounds) return item_of(r);
+    const int slot = r & 3;
+    int item = total;
+    if (lane == 0) {
+      const int old = __hip_atomic_fetch_max(&s_claim_busy[slot], r, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (old < r) {
+        const int x = bid % kClaimPools;
+        const int j = __hip_atomic_fetch_add(&a.ws_ctrl[kCtrlClaims + x * kClaimStride], 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t cand = (int64_t)NG + x + (int64_t)j * kClaimPools;
+        item = cand < total ? (int)cand : total;
+        s_claim_item[slot] = item;
+        __hip_atomic_store(&s_claim_tag[slot], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        bool published = true;
+        for (int spin = 0; __hip_atomic_load(&s_claim_tag[slot], __ATOMIC_ACQUIRE,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP) != r; ++spin) {
+          if (spin == kSpinLimit) {
+            abort_wait();
+            published = false;   // end this wave's stream
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (published) item = s_claim_item[slot];
+      }
+    }
+    return __builtin_amdgcn_readfirstlane(item);
+  };
 
   auto desc = [&](int r) -> Desc {
     Desc d;
-    const int item = item_of(r);
+    const int item = item_for(r);
     d.valid = item < total;
     const int e_idx = d.valid ? item / Hkv : 0;
     d.s = items[4 * e_idx + 0];
@@ -851,6 +900,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   if (threadIdx.x < kMaxLdsSlots) {
     s_count[threadIdx.x] = 0;
     s_epoch[threadIdx.x] = threadIdx.x;
+  }
+  if (threadIdx.x < 4) {
+    s_claim_busy[threadIdx.x] = -1;
+    s_claim_tag[threadIdx.x] = -1;
   }
   __syncthreads();
   Desc cur = desc(0);

@@ -60,7 +60,13 @@ constexpr int kCtrlPrefixPart = 4;    // blocks per prefix partition
 // workgroup did not end (a broken invariant; the output is then incomplete).
 // Tests read it; cleared by the planner.
 constexpr int kCtrlAbort = 20;
-constexpr int kCtrlSize = 32;
+// Claim counters of the matrix-core kernel's work list, one per pool
+// (workgroups b with b % kClaimPools == x claim from pool x), each in a
+// 128-byte line of its own; zeroed by the planner.
+constexpr int kClaimPools = 32;
+constexpr int kClaimStride = 32;
+constexpr int kCtrlClaims = 32;
+constexpr int kCtrlSize = kCtrlClaims + kClaimPools * kClaimStride;
 
 enum class KvType { F32 = 0, BF16 = 1 };
 

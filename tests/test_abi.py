@@ -56,14 +56,18 @@ def _align(n):
     return (n + 255) // 256 * 256
 
 
+# planner control words: 32 ints + 8 claim counters, each in its own 128-byte line
+CTRL = 1280
+
+
 def test_workspace_sizes(lib):
     # one partition per sequence: planner outputs + work list + split list only
     assert lib.pa_decode_workspace_bytes_ex(4, 8, 8, 64, 4, 16, 0, 64) == \
-        256 + _align(4 * 1 * 16) + _align(4 * 8)
+        CTRL + _align(4 * 1 * 16) + _align(4 * 8)
     # 256 seqs, 64 heads / 8 KV heads, D=128, 285 blocks of 16, 512-token partitions -> 9
     n = lib.pa_decode_workspace_bytes_ex(256, 64, 8, 128, 285, 16, 1, 512)
     rows = 256 * 64 * 9
-    assert n == (256 + _align(256 * 9 * 16) + _align(256 * 8) + _align(rows * 128 * 4) +
+    assert n == (CTRL + _align(256 * 9 * 16) + _align(256 * 8) + _align(rows * 128 * 4) +
                  _align(rows * 8))
     # the library's choice is sized for its smallest partition (256 tokens)
     assert lib.pa_decode_workspace_bytes(256, 64, 8, 128, 285, 16, 1) == \
@@ -172,7 +176,7 @@ def test_shared_prefix_workspace_and_errors(lib):
     parts = 11 + 1                # ceil(161 / 16) partitions, + 1 for the prefix cut
     rows = 128 * 32 * parts       # S * Hq * partitions
     n = lib.pa_decode_shared_prefix_workspace_bytes(128, 32, 8, 128, 161, 16, 1, 256)
-    assert n == 256 + _align(128 * parts * 16) + _align(128 * 8) + _align(rows * 128 * 4) + \
+    assert n == CTRL + _align(128 * parts * 16) + _align(128 * 8) + _align(rows * 128 * 4) + \
         _align(rows * 8) + _align(128 * parts * 16)
     assert lib.pa_decode_shared_prefix_workspace_bytes(4, 6, 4, 64, 4, 16, 1, 0) == 0
     FAKE = 1 << 40
