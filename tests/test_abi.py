@@ -56,8 +56,8 @@ def _align(n):
     return (n + 255) // 256 * 256
 
 
-# planner control words: 32 ints + 8 claim counters, each in its own 128-byte line
-CTRL = 1280
+# planner control words: 32 ints + 32 claim counters, each in its own 128-byte line
+CTRL = _align((32 + 32 * 32) * 4)
 
 
 def test_workspace_sizes(lib):
