@@ -175,7 +175,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *   block_tables   [num_seqs, max_blocks_per_seq] int32, device; entries past
  *                  ceil(L / block_size) are never read (padding, e.g. -1)
  *   context_lens   [num_seqs] int32, device
- *   workspace      device, at least pa_decode_workspace_bytes(...) bytes
+ *   workspace      device, 256-byte aligned, at least
+ *                  pa_decode_workspace_bytes(...) bytes (else PA_ERR_WORKSPACE)
  *   num_seqs == 0 is a successful no-op.
  * Compiled: head_dim in {64, 128}, block_size in {16, 32}, group size
  * num_heads / num_kv_heads in [1, 16], kv_dtype F32 or BF16.

@@ -196,6 +196,8 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
   if (!workspace || workspace_bytes < lay.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed",
                 workspace_bytes, workspace, lay.total);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(PA_ERR_WORKSPACE, "workspace at %p must be 256-byte aligned", workspace);
   if ((int64_t)lay.num_parts_max * num_seqs * num_kv_heads > (INT32_MAX >> 1) ||
       (int64_t)max_blocks_per_seq * num_seqs > (INT32_MAX >> 1))
     return fail(PA_ERR_UNSUPPORTED, "too many work items");

@@ -26,8 +26,9 @@
 //                 round in snake order), so no workgroup is launched for an
 //                 empty partition and the workgroups end close together
 //                 however ragged the context lengths are.
-//   merge_splits  log-sum-exp merge, in partition order, of the partition
-//                 states of every sequence listed by the planner.
+//   merge_splits  log-sum-exp merge of the partition states of every
+//                 sequence listed by the planner: per-head maxima and sums
+//                 first, then the weighted sum of the partitions' vectors.
 //
 // Inside an item, the wave in lane j of the W lanes takes logical blocks
 // b0 + j, b0 + j + W, ... and keeps a running softmax state (max m, sum l,
@@ -152,12 +153,15 @@ __device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
 constexpr int kPartChoices = 8;
 
 constexpr int kLensCached = 8192;   // context lengths the planner keeps in LDS
+constexpr int kDirectItems = 4;     // full partitions a planner thread lists itself
 
 __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size) {
   __shared__ int lens_c[kLensCached];
   __shared__ int start_c[kLensCached];   // shared-prefix blocks per sequence
   __shared__ int cls_off[kTailClasses];
   __shared__ int wave_sum[16];
+  __shared__ int chunk_incl[1024];
+  __shared__ int long_seen;
   __shared__ int run_base;
   __shared__ int nsplit;
   __shared__ int npitems;
@@ -168,6 +172,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   for (int i = tid; i < kTailClasses; i += 1024) cls_off[i] = 0;
   if (tid == 0) {
     run_base = 0;
+    long_seen = 0;
     nsplit = 0;
     npitems = 0;
   }
@@ -271,16 +276,39 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       if (lane >= off) incl += v;
     }
     if (lane == 63) wave_sum[wave] = incl;
+    if (nfull > kDirectItems) long_seen = 1;
     __syncthreads();
     int before = 0, chunk = 0;
     for (int w = 0; w < 16; ++w) {
       before += w < wave ? wave_sum[w] : 0;
       chunk += wave_sum[w];
     }
+    // A sequence's first kDirectItems full partitions are listed by its own
+    // thread.  Any further ones (long contexts) are listed by all threads,
+    // each finding its sequence by binary search over the chunk's inclusive
+    // counts: one thread listing a hundred partitions took microseconds.
     const int base = run_base + before + incl - nfull;
-    for (int p = 0; p < nfull; ++p) a.ws_items[base + p] = make_int4(s, p, L, P);
+    for (int p = 0; p < min(nfull, kDirectItems); ++p) a.ws_items[base + p] = make_int4(s, p, L, P);
+    chunk_incl[tid] = before + incl;
     __syncthreads();
-    if (tid == 0) run_base += chunk;
+    if (long_seen) {
+      for (int i = tid; i < chunk; i += 1024) {
+        int lo = 0, hi = min(S - c0, 1024) - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (chunk_incl[mid] > i) hi = mid; else lo = mid + 1;
+        }
+        const int p = i - (lo > 0 ? chunk_incl[lo - 1] : 0);
+        const int sq = c0 + lo;
+        if (p >= kDirectItems)
+          a.ws_items[run_base + i] = make_int4(sq, p, len_of(sq), start_of(sq));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      run_base += chunk;
+      long_seen = 0;
+    }
     __syncthreads();
   }
 
@@ -1289,49 +1317,155 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 // head) at a time, four features per thread.
 // ---------------------------------------------------------------------------
 
+// Log-sum-exp merge of a split sequence's partition states (m_p, l_p, acc_p),
+// per query head g:  M = max_p m_p,  lambda = sum_p l_p 2^(m_p - M),
+// out = (sum_p acc_p 2^(m_p - M)) / lambda  (m in base-2 units).
+// One workgroup per (split sequence, KV head).  With at most kMergeBatch
+// partitions, each (head, 4 features) column's thread loads them all and
+// merges them alone.  Otherwise wave g % kMergeWaves finds
+// M and lambda of head g over lane-strided partitions; rows of threads take
+// contiguous runs of partitions of one (head, 4 features) column for the
+// weighted sum, whose terms do not depend on one another, and the rows'
+// partial sums are added in row order.  A unit's loads (its first
+// kMergeBatch partitions per row, kMergeHeld * 64 (m, l) pairs per head)
+// are all issued before any reduction, so a call costs few memory round
+// trips however many partitions a sequence has.  Every order depends only on
+// the partition count, so results are reproducible.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeThreads = 64 * kMergeWaves;
+constexpr int kMergeBatch = 16;
+constexpr int kMergeHeld = 2;
+constexpr int kMergeGrid = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits(DecodeParams a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
-  constexpr int kBatch = 4;
+  constexpr int kCols4 = D / 4;
+  __shared__ float head_max[kMaxGroup], head_sum[kMaxGroup];
+  __shared__ f4 partial[kMergeThreads];
   const int Hkv = a.num_kv_heads, G = a.group;
-  // One thread per (split sequence, KV head, query head of the group, 4 features).
-  const int per_seq = Hkv * G * (D / 4);
-  const int64_t total = (int64_t)a.ws_ctrl[kCtrlSplits] * per_seq;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int e_idx = (int)(idx / per_seq);
-    const int rem = (int)(idx - (int64_t)e_idx * per_seq);
-    const int h = rem / (G * (D / 4));
-    const int g = (rem / (D / 4)) % G;
-    const int d4 = rem % (D / 4);
-    const int2 e = a.ws_split[e_idx];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = G * kCols4;                       // (head, 4 features) columns, <= 512
+  const int R = kMergeThreads / C;                // rows of partitions per column, >= 1
+  const int r = tid / C, c = tid - r * C;
+  const int g = c / kCols4, d4 = c - g * kCols4;  // this thread's column
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const int64_t units = (int64_t)a.num_seqs * Hkv;   // ws_split has num_seqs entries
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int2 e = a.ws_split[u / Hkv];
+    if (u >= (int64_t)a.ws_ctrl[kCtrlSplits] * Hkv) break;
+    const int h = (int)(u % Hkv);
     const int s = e.x, nparts = e.y;
-    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
-    float M = kNegInf, lam = 0.f;
-    f4 val = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < nparts; p0 += kBatch) {
-      float mp[kBatch], lp[kBatch];
-      f4 ap[kBatch];
+    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;   // partition 0's row
+    float* const out_col = a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4;
+    if (nparts <= kMergeBatch) {
+      // Few partitions: each column's thread loads all of them at once and
+      // merges them alone (no barrier, no exchange between threads).
+      if (r == 0) {
+        float2 mlp[kMergeBatch];
+        f4 ap[kMergeBatch];
+        float M = kNegInf;
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int64_t row = (prow + min(p0 + j, nparts - 1)) * G + g;
-        mp[j] = a.ws_ml[row * 2];
-        lp[j] = a.ws_ml[row * 2 + 1];
-        ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const int64_t row = (prow + min(j, nparts - 1)) * G + g;
+          mlp[j] = j < nparts ? ml[row] : make_float2(kNegInf, 0.f);
+          ap[j] = j < nparts ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
+                             : f4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) M = fmaxf(M, mlp[j].x);
+        float lam = 0.f;
+        f4 val = {0.f, 0.f, 0.f, 0.f};
+        if (M != kNegInf) {
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j)
+            if (mlp[j].x != kNegInf) {
+              const float w = exp2_fast(mlp[j].x - M);
+              lam += mlp[j].y * w;
+              val += ap[j] * w;
+            }
+        }
+        *reinterpret_cast<f4*>(out_col) = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
+      }
+      continue;
+    }
+    const int p_lo = (int)((int64_t)nparts * r / R), p_hi = (int)((int64_t)nparts * (r + 1) / R);
+    const bool sums = r < R;
+    // Issue this unit's loads: the first batch of the weighted sum, and the
+    // (m, l) pairs the wave reduces.
+    float mp[kMergeBatch];
+    f4 ap[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int64_t row = (prow + max(min(min(p_lo + j, p_hi - 1), nparts - 1), 0)) * G + g;
+      mp[j] = sums && p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
+      ap[j] = sums && p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
+                                      : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    float2 held[kMergeHeld];
+    const int g1 = wave < G ? wave : 0;
+#pragma unroll
+    for (int j = 0; j < kMergeHeld; ++j) {
+      const int p = lane + 64 * j;
+      held[j] = wave < G && p < nparts ? ml[(prow + p) * G + g1] : make_float2(kNegInf, 0.f);
+    }
+    for (int gg = wave; gg < G; gg += kMergeWaves) {
+      float m = kNegInf;
+      if (gg == wave) {
+#pragma unroll
+        for (int j = 0; j < kMergeHeld; ++j) m = fmaxf(m, held[j].x);
+      }
+      for (int p = lane + (gg == wave ? 64 * kMergeHeld : 0); p < nparts; p += 64)
+        m = fmaxf(m, ml[(prow + p) * G + gg].x);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+      float l = 0.f;
+      if (m != kNegInf) {
+        if (gg == wave) {
+#pragma unroll
+          for (int j = 0; j < kMergeHeld; ++j)
+            if (held[j].x != kNegInf) l += held[j].y * exp2_fast(held[j].x - m);
+        }
+        for (int p = lane + (gg == wave ? 64 * kMergeHeld : 0); p < nparts; p += 64) {
+          const float2 v = ml[(prow + p) * G + gg];
+          if (v.x != kNegInf) l += v.y * exp2_fast(v.x - m);
+        }
       }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (p0 + j >= nparts) break;
-        const float Mn = fmaxf(M, mp[j]);
-        if (Mn == kNegInf) continue;        // nothing live yet
-        const float cold = exp2_fast(M - Mn), cnew = exp2_fast(mp[j] - Mn);
-        lam = lam * cold + lp[j] * cnew;
-        val = val * cold + ap[j] * cnew;
-        M = Mn;
+      for (int off = 1; off < 64; off <<= 1) l += shfl_xor_f(l, off);
+      if (lane == 0) {
+        head_max[gg] = m;
+        head_sum[gg] = l;
       }
     }
-    const f4 o = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) = o;
+    __syncthreads();
+    f4 val = {0.f, 0.f, 0.f, 0.f};
+    if (sums && head_max[g] != kNegInf) {
+      const float M = head_max[g];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
+      for (int p0 = p_lo + kMergeBatch; p0 < p_hi; p0 += kMergeBatch) {
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+          const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + g;
+          mp[j] = a.ws_ml[row * 2];
+          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j)
+          if (p0 + j < p_hi && mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
+      }
+    }
+    partial[tid] = val;
+    __syncthreads();
+    if (tid < C) {
+      f4 sum = partial[tid];
+      for (int rr = 1; rr < R; ++rr) sum += partial[rr * C + tid];
+      const float lam = head_sum[g];
+      *reinterpret_cast<f4*>(out_col) = lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();   // head_max, head_sum and partial are reused by the next unit
   }
 }
 
@@ -1446,12 +1580,14 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
   if (p.num_parts_max <= 1) return hipSuccess;
-  // Enough threads for every (sequence, head, 4 features) of a full batch of
-  // split sequences, up to 4 workgroups per CU; the kernel loops past that.
-  const int64_t threads_needed = (int64_t)p.num_seqs * p.num_heads * (D / 4);
-  const int64_t mblocks = (threads_needed + 255) / 256;
-  const unsigned mgrid = (unsigned)(mblocks < 1024 ? mblocks : 1024);
-  hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(256), 0, stream, p);
+  // One workgroup per (sequence, KV head) of a batch whose every sequence is
+  // split, up to kMergeGrid; the kernel loops past that.  Only the planner
+  // knows how many sequences are split; a workgroup beyond that count still
+  // occupies its wave slots for a memory round trip before it exits, so the
+  // grid is kept small.
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
+  const unsigned mgrid = (unsigned)(units < kMergeGrid ? units : kMergeGrid);
+  hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -110,6 +110,7 @@ def _decode(lib, **kw):
     (dict(dt=7), 2),
     (dict(ws=None, maxb=100), 3),
     (dict(wsb=16, maxb=100), 3),
+    (dict(ws=FAKE + 16), 3),
 ])
 def test_decode_rejects_bad_arguments(lib, kw, status):
     assert _decode(lib, **kw) == status
