@@ -164,6 +164,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   __shared__ int long_seen;
   __shared__ int run_base;
   __shared__ int nsplit;
+  __shared__ int nsplit_long;
   __shared__ int npitems;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.num_seqs;
@@ -174,6 +175,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     run_base = 0;
     long_seen = 0;
     nsplit = 0;
+    nsplit_long = 0;
     npitems = 0;
   }
   // One pass over the context lengths (clamped), kept in LDS for the passes
@@ -266,8 +268,11 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       if (c >= 0) atomicAdd(&cls_off[c], 1);
       const int nown = (nblk + pb - 1) / pb;
       const int npre = (P + pbp - 1) / pbp;
-      if (npre + nown > 1 || npre > 0)
-        a.ws_split[atomicAdd(&nsplit, 1)] = make_int2(s, npre + nown);
+      if (npre + nown > 1 || npre > 0) {
+        const int at = npre + nown <= kMergeShort ? atomicAdd(&nsplit, 1)
+                                                  : S - 1 - atomicAdd(&nsplit_long, 1);
+        a.ws_split[at] = make_int2(s, npre + nown);
+      }
     }
     int incl = nfull;
 #pragma unroll
@@ -331,6 +336,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       if (tid == kTailClasses - 1) {
         a.ws_ctrl[kCtrlEntries] = before + incl;
         a.ws_ctrl[kCtrlSplits] = nsplit;
+        a.ws_ctrl[kCtrlLongSplits] = nsplit_long;
       }
     }
     __syncthreads();
@@ -1320,22 +1326,27 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 // Log-sum-exp merge of a split sequence's partition states (m_p, l_p, acc_p),
 // per query head g:  M = max_p m_p,  lambda = sum_p l_p 2^(m_p - M),
 // out = (sum_p acc_p 2^(m_p - M)) / lambda  (m in base-2 units).
-// One workgroup per (split sequence, KV head).  With at most kMergeBatch
-// partitions, each (head, 4 features) column's thread loads them all and
-// merges them alone.  Otherwise wave g % kMergeWaves finds
-// M and lambda of head g over lane-strided partitions; rows of threads take
-// contiguous runs of partitions of one (head, 4 features) column for the
-// weighted sum, whose terms do not depend on one another, and the rows'
-// partial sums are added in row order.  A unit's loads (its first
-// kMergeBatch partitions per row, kMergeHeld * 64 (m, l) pairs per head)
-// are all issued before any reduction, so a call costs few memory round
-// trips however many partitions a sequence has.  Every order depends only on
-// the partition count, so results are reproducible.
+// A unit is one (split sequence, KV head); a column is one (query head,
+// 4 features) of it.  The planner lists sequences with at most kMergeShort
+// partitions apart from longer ones.
+//   Short units: one thread per column loads all of the unit's partitions at
+//   once and merges them alone, with no barrier.  Unit u goes to workgroup
+//   u % grid, row (u / grid) % R of its R = threads / C rows of C columns:
+//   units spread over all workgroups before any takes a second one.
+//   Long units: one workgroup per unit, the last workgroups first.  Wave g % kMergeWaves finds M and
+//   lambda of head g over lane-strided partitions; rows of threads take
+//   contiguous runs of partitions of one column for the weighted sum, whose
+//   terms do not depend on one another, and the rows' partial sums are added
+//   in row order.  A unit's first loads (kMergeBatch partitions per row,
+//   kMergeHeld * 64 (m, l) pairs per head) are issued before any reduction.
+// Every order depends only on the partition count, so results are
+// reproducible.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = 64 * kMergeWaves;
 constexpr int kMergeBatch = 16;
 constexpr int kMergeHeld = 2;
 constexpr int kMergeGrid = 256;
+static_assert(kMergeShort <= kMergeBatch, "a short unit's partitions are loaded in one batch");
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
@@ -1343,56 +1354,57 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   constexpr int kCols4 = D / 4;
   __shared__ float head_max[kMaxGroup], head_sum[kMaxGroup];
   __shared__ f4 partial[kMergeThreads];
-  const int Hkv = a.num_kv_heads, G = a.group;
+  const int Hkv = a.num_kv_heads, G = a.group, S = a.num_seqs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int C = G * kCols4;                       // (head, 4 features) columns, <= 512
-  const int R = kMergeThreads / C;                // rows of partitions per column, >= 1
+  const int C = G * kCols4;                       // columns per unit, <= 512
+  const int R = kMergeThreads / C;                // rows of threads, >= 1
   const int r = tid / C, c = tid - r * C;
   const int g = c / kCols4, d4 = c - g * kCols4;  // this thread's column
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
-  const int64_t units = (int64_t)a.num_seqs * Hkv;   // ws_split has num_seqs entries
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int2 e = a.ws_split[u / Hkv];
-    if (u >= (int64_t)a.ws_ctrl[kCtrlSplits] * Hkv) break;
+  const int64_t n_short = (int64_t)a.ws_ctrl[kCtrlSplits] * Hkv;
+  const int64_t n_long = (int64_t)a.ws_ctrl[kCtrlLongSplits] * Hkv;
+
+  if (r < R) {
+    for (int64_t u = blockIdx.x + (int64_t)r * gridDim.x; u < n_short; u += (int64_t)gridDim.x * R) {
+      const int2 e = a.ws_split[u / Hkv];
+      const int h = (int)(u % Hkv);
+      const int s = e.x, nparts = e.y;
+      const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;   // partition 0's row
+      float2 mlp[kMergeShort];
+      f4 ap[kMergeShort];
+      float M = kNegInf;
+#pragma unroll
+      for (int j = 0; j < kMergeShort; ++j) {
+        const int64_t row = (prow + min(j, nparts - 1)) * G + g;
+        mlp[j] = j < nparts ? ml[row] : make_float2(kNegInf, 0.f);
+        ap[j] = j < nparts ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
+                           : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeShort; ++j) M = fmaxf(M, mlp[j].x);
+      float lam = 0.f;
+      f4 val = {0.f, 0.f, 0.f, 0.f};
+      if (M != kNegInf) {
+#pragma unroll
+        for (int j = 0; j < kMergeShort; ++j)
+          if (mlp[j].x != kNegInf) {
+            const float w = exp2_fast(mlp[j].x - M);
+            lam += mlp[j].y * w;
+            val += ap[j] * w;
+          }
+      }
+      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) =
+          lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  for (int64_t u = gridDim.x - 1 - blockIdx.x; u < n_long; u += gridDim.x) {
+    const int2 e = a.ws_split[S - 1 - u / Hkv];
     const int h = (int)(u % Hkv);
     const int s = e.x, nparts = e.y;
-    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;   // partition 0's row
-    float* const out_col = a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4;
-    if (nparts <= kMergeBatch) {
-      // Few partitions: each column's thread loads all of them at once and
-      // merges them alone (no barrier, no exchange between threads).
-      if (r == 0) {
-        float2 mlp[kMergeBatch];
-        f4 ap[kMergeBatch];
-        float M = kNegInf;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-          const int64_t row = (prow + min(j, nparts - 1)) * G + g;
-          mlp[j] = j < nparts ? ml[row] : make_float2(kNegInf, 0.f);
-          ap[j] = j < nparts ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
-                             : f4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) M = fmaxf(M, mlp[j].x);
-        float lam = 0.f;
-        f4 val = {0.f, 0.f, 0.f, 0.f};
-        if (M != kNegInf) {
-#pragma unroll
-          for (int j = 0; j < kMergeBatch; ++j)
-            if (mlp[j].x != kNegInf) {
-              const float w = exp2_fast(mlp[j].x - M);
-              lam += mlp[j].y * w;
-              val += ap[j] * w;
-            }
-        }
-        *reinterpret_cast<f4*>(out_col) = lam > 0.f ? val / lam : f4{0.f, 0.f, 0.f, 0.f};
-      }
-      continue;
-    }
+    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
     const int p_lo = (int)((int64_t)nparts * r / R), p_hi = (int)((int64_t)nparts * (r + 1) / R);
     const bool sums = r < R;
-    // Issue this unit's loads: the first batch of the weighted sum, and the
-    // (m, l) pairs the wave reduces.
     float mp[kMergeBatch];
     f4 ap[kMergeBatch];
 #pragma unroll
@@ -1463,7 +1475,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
       f4 sum = partial[tid];
       for (int rr = 1; rr < R; ++rr) sum += partial[rr * C + tid];
       const float lam = head_sum[g];
-      *reinterpret_cast<f4*>(out_col) = lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) =
+          lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();   // head_max, head_sum and partial are reused by the next unit
   }

@@ -37,7 +37,8 @@ struct DecodeParams {
   float* ws_ml;               // [S, Hkv, num_parts_max, group, 2] partition (max, sum)
   int4* ws_items;             // [S * num_parts_max] work list: (sequence, partition, length,
                               //  first block: the sequence's shared-prefix blocks, else 0)
-  int2* ws_split;             // [S] (sequence, partitions) of sequences spanning several
+  int2* ws_split;             // [S] (sequence, partitions) of sequences spanning several:
+                              //  up to kMergeShort partitions from the front, more from the back
   int32_t* ws_ctrl;           // [kCtrlSize] written by the planner
   // Shared prefixes (num_groups == 0: none).  Sequences group_starts[g] ..
   // group_starts[g+1]-1 share their first prefix_blocks[g] table entries.
@@ -56,6 +57,9 @@ constexpr int kCtrlPartBlocks = 1;
 constexpr int kCtrlSplits = 2;
 constexpr int kCtrlPrefixItems = 3;   // entries of the prefix work list
 constexpr int kCtrlPrefixPart = 4;    // blocks per prefix partition
+constexpr int kCtrlLongSplits = 5;    // split sequences with more than kMergeShort partitions,
+                                      // listed from the back of ws_split
+constexpr int kMergeShort = 16;
 // Set by the decode kernel if one of its waits on other waves of its
 // workgroup did not end (a broken invariant; the output is then incomplete).
 // Tests read it; cleared by the planner.
