@@ -849,8 +849,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // The workgroup's item for round r.  The list (longest items first) is
   // dealt, in snake order, for the first round only -- item b to workgroup
   // b -- and claimed after that: workgroup b takes the next unclaimed item of
-  // pool x = b % kClaimPools (items NG + x, NG + x + kClaimPools, ...) until
-  // the pool is empty.  The two workgroups sharing a CU stream at different
+  // pool x = (b / 2) % kClaimPools (items NG + x, NG + x + kClaimPools, ...)
+  // until the pool is empty.  The two workgroups sharing a CU stream at different
   // speeds (the first dispatched one gets most of the memory pipeline), and
   // so do CUs on more or less loaded memory paths; claiming lets the faster
   // ones take more of the list, so the workgroups end closer together.
@@ -858,7 +858,15 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // 209.3 us per call with every round dealt in snake order, 204.4 us with 8
   // pools, 199.7 us with 32 (contention on each counter falls), 200.5 us with
   // 64, 202.3 us with 128 (a pool's items are shared by fewer workgroups);
-  // claiming the first round too, 201.5 us.  The first wave to need round
+  // claiming the first round too, 201.5 us.  Workgroups are dispatched to
+  // the 8 XCDs round-robin (b % 8), so pools x = b % 32 each lived on one XCD
+  // and an XCD with slower memory paths still did an eighth of the list
+  // (per-workgroup end times: XCD medians 184.5 to 194.0 us); with x =
+  // (b / 2) % 32 each pool spans two XCDs: 201.9 vs 203.7 us on one host
+  // (x = (b / 8) % 32, all eight XCDs per pool: 203.0 us).  Letting a
+  // workgroup whose pool is empty claim from other pools cost more than it
+  // saved (a scan of the pools' counters before a workgroup may end: large
+  // batch +1 us, small batches +2 to +3 us).  The first wave to need round
   // r's item claims it (one device-scope atomic) and publishes it in LDS for
   // the other waves.  Who computes an item never changes its result.  With
   // fewer than two rounds of items every round is dealt in snake order
@@ -869,34 +877,47 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   __shared__ int s_claim_busy[4];   // last round whose claim was started
   __shared__ int s_claim_tag[4];    // last round whose claim is published
   __shared__ int s_claim_item[4];
+  int32_t* const claims = a.ws_ctrl + kCtrlClaims;
+  // One claim from pool y by lane 0, returned to the whole wave.
+  auto claim_from = [&](int y) -> int {
+    int it = total;
+    if (lane == 0) {
+      const int j = __hip_atomic_fetch_add(&claims[y * kClaimStride], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      const int64_t cand = (int64_t)NG + y + (int64_t)j * kClaimPools;
+      it = cand < total ? (int)cand : total;
+    }
+    return __builtin_amdgcn_readfirstlane(it);
+  };
   auto item_for = [&](int r) -> int {
     if (r == 0 || !claimed_rounds) return item_of(r);
     const int slot = r & 3;
-    int item = total;
-    if (lane == 0) {
-      const int old = __hip_atomic_fetch_max(&s_claim_busy[slot], r, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (old < r) {
-        const int x = bid % kClaimPools;
-        const int j = __hip_atomic_fetch_add(&a.ws_ctrl[kCtrlClaims + x * kClaimStride], 1,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int64_t cand = (int64_t)NG + x + (int64_t)j * kClaimPools;
-        item = cand < total ? (int)cand : total;
+    int claimer = 0;
+    if (lane == 0)
+      claimer = __hip_atomic_fetch_max(&s_claim_busy[slot], r, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP) < r;
+    if (__builtin_amdgcn_readfirstlane(claimer)) {
+      const int x = (bid >> 1) & (kClaimPools - 1);
+      const int item = claim_from(x);
+      if (lane == 0) {
         s_claim_item[slot] = item;
         __hip_atomic_store(&s_claim_tag[slot], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
-        bool published = true;
-        for (int spin = 0; __hip_atomic_load(&s_claim_tag[slot], __ATOMIC_ACQUIRE,
-                                             __HIP_MEMORY_SCOPE_WORKGROUP) != r; ++spin) {
-          if (spin == kSpinLimit) {
-            abort_wait();
-            published = false;   // end this wave's stream
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (published) item = s_claim_item[slot];
       }
+      return item;
+    }
+    int item = total;
+    if (lane == 0) {
+      bool published = true;
+      for (int spin = 0; __hip_atomic_load(&s_claim_tag[slot], __ATOMIC_ACQUIRE,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP) != r; ++spin) {
+        if (spin == kSpinLimit) {
+          abort_wait();
+          published = false;   // end this wave's stream
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (published) item = s_claim_item[slot];
     }
     return __builtin_amdgcn_readfirstlane(item);
   };
