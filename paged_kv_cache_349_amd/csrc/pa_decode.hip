@@ -137,17 +137,23 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& a, int s, int block
 // Work list.
 // ---------------------------------------------------------------------------
 
-// Block-wide sum over the planner's 1024 threads (16 waves).
+// Sum over each 16-lane row of a wave (every lane of the row gets it).
+__device__ __forceinline__ int row16_sum(int v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Block-wide sum over the planner's 1024 threads (16 waves).  The 16 wave
+// sums are read with one LDS load per lane and added across lanes, not by
+// 16 dependent loads.
 __device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) scratch16[threadIdx.x >> 6] = v;
   __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) t += scratch16[w];
-  return t;
+  return row16_sum(scratch16[threadIdx.x & 15]);
 }
 
 constexpr int kPartChoices = 8;
@@ -210,7 +216,8 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       pre_mine += (hi - lo + per_item - 1) / per_item * P;
     }
   }
-  const int64_t pre_total = block_sum_1024(pre_mine, wave_sum);   // also publishes start_c
+  // (The sum's barriers also publish start_c.)
+  const int64_t pre_total = prefix ? block_sum_1024(pre_mine, wave_sum) : 0;
   int mine = 0;
   for (int s = tid; s < S; s += 1024)
     mine += (len_of(s) + block_size - 1) / block_size - start_of(s);
@@ -249,7 +256,8 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   auto tail_class = [&](int nblk) {
     const int rem = nblk % pb;
     if (rem == 0) return -1;
-    return (int)((int64_t)(pb - rem) * (kTailClasses - 1) / pb);
+    return pb < (1 << 23) ? (pb - rem) * (kTailClasses - 1) / pb
+                          : (int)((int64_t)(pb - rem) * (kTailClasses - 1) / pb);
   };
 
   // Pass 1: full partitions in sequence order (an empty sequence gets one
@@ -283,11 +291,9 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     if (lane == 63) wave_sum[wave] = incl;
     if (nfull > kDirectItems) long_seen = 1;
     __syncthreads();
-    int before = 0, chunk = 0;
-    for (int w = 0; w < 16; ++w) {
-      before += w < wave ? wave_sum[w] : 0;
-      chunk += wave_sum[w];
-    }
+    const int wsum = wave_sum[lane & 15];
+    const int chunk = row16_sum(wsum);
+    const int before = row16_sum((lane & 15) < wave ? wsum : 0);
     // A sequence's first kDirectItems full partitions are listed by its own
     // thread.  Any further ones (long contexts) are listed by all threads,
     // each finding its sequence by binary search over the chunk's inclusive
