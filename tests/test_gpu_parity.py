@@ -301,3 +301,21 @@ def test_decode_step_empty_parts():
     torch.cuda.synchronize()
     from paged_kv_cache_349_amd.device_io import torch_to_np
     assert np.array_equal(torch_to_np(e.k_cache, "f32").view(np.uint32), k_ref.view(np.uint32))
+
+
+def test_many_sequences_past_the_planner_cache():
+    """9000 sequences: more than the planner keeps in LDS (8192) and more than one
+    chunk of its 1024 threads; lengths 0..39 plus two long ones that split."""
+    rng = np.random.default_rng(7)
+    lens = list(rng.integers(0, 40, size=9000))
+    lens[5], lens[8500] = 5000, 3000
+    w = _custom(lens, 8, 2, 64, 16, "bf16", seed=9)
+    _say(f"S={w.num_seqs} NB={w.num_blocks} max_blocks={w.max_blocks}")
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, 16, "bf16")
+    for pt in (0, 64):
+        out = _run(w, partition_tokens=pt).out.cpu().numpy()
+        err = float(np.abs(out - ref).max())
+        _say(f"  partition_tokens={pt} max-abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.all(out[np.asarray(lens) == 0] == 0.0)
