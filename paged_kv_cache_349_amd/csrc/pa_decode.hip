@@ -80,6 +80,7 @@ constexpr int kTailClasses = 256;
 constexpr int kMaxLdsSlots = 2;    // LDS state slots of the matrix-core kernel (power of 2)
 constexpr int kMaxLdsRecords = 16; // LDS output records of the matrix-core kernel
 constexpr int kSpinLimit = 1 << 22; // polls (~0.1 s) before an LDS wait is declared broken
+constexpr int kLateStop = 8;        // items of a claim pool left to the first workgroups
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -904,6 +905,30 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
                                        __HIP_MEMORY_SCOPE_WORKGROUP) < r;
     if (__builtin_amdgcn_readfirstlane(claimer)) {
       const int x = (bid >> 1) & (kClaimPools - 1);
+      if (bid >= a.num_cus) {
+        // A workgroup dispatched after its CU's first one streams slower
+        // (timestamps: the last workgroups to end were all of these); it
+        // leaves a pool's last kLateStop items to the first workgroups, which
+        // claim until the pool is empty.  Same host, alternating builds, kernel
+        // with kLateStop 0 / 4 / 8 / 16: gqa 54.0 / 52.2 / 51.5 / 51.5 us,
+        // parallel sampling (shared prefix) 55.6 / 54.2 / 54.5 / 55.0 us,
+        // large batch 189.1 / 189.2 / 189.1 / 189.0 us.
+        int stop = 0;
+        if (lane == 0) {
+          const int64_t left = (int64_t)total - NG - x;
+          const int64_t size = left > 0 ? (left + kClaimPools - 1) / kClaimPools : 0;
+          const int j = __hip_atomic_load(&claims[x * kClaimStride], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+          stop = size - j < kLateStop;
+        }
+        if (__builtin_amdgcn_readfirstlane(stop)) {
+          if (lane == 0) {
+            s_claim_item[slot] = total;
+            __hip_atomic_store(&s_claim_tag[slot], r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+          return total;
+        }
+      }
       const int item = claim_from(x);
       if (lane == 0) {
         s_claim_item[slot] = item;
@@ -1537,6 +1562,21 @@ void lds_layout_for(int group, int* slots, int* records) {
   *records = nr;
 }
 
+// Compute units of the current device (0 if unknown).
+int cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto found = cache.find(dev);
+  if (found != cache.end()) return found->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  cache.emplace(dev, cus);
+  return cus;
+}
+
 // Workgroups of `kernel` that fit on the current device at once.
 int resident_workgroups(const void* kernel, int threads, size_t smem) {
   static std::mutex mu;
@@ -1588,6 +1628,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (resident <= 0) return hipErrorInvalidDeviceFunction;
   const int64_t max_items = (int64_t)p.num_seqs * p.num_parts_max * p.num_kv_heads;
   p.decode_grid = (int)(max_items < resident ? max_items : resident);
+  p.num_cus = cu_count();
 
   p.prefix_rows = kPrefixRows;
   if (write && write->total > 0) {

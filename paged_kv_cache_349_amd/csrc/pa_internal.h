@@ -31,6 +31,7 @@ struct DecodeParams {
                               // workgroup's share of the work (0: always part_blocks_min;
                               // the API sets 1 for adaptive, the launcher the ratio)
   int32_t decode_grid;        // workgroups of the decode launch (set by the launcher)
+  int32_t num_cus;            // compute units of the device (set by the launcher)
   int32_t lds_slots;          // LDS state slots of the matrix-core kernel (set by the launcher)
   int32_t lds_records;        // LDS output records of the matrix-core kernel (set by the launcher)
   float* ws_acc;              // [S, Hkv, num_parts_max, group, D] partition sums
