@@ -30,8 +30,9 @@
 //                 sequence listed by the planner: per-head maxima and sums
 //                 first, then the weighted sum of the partitions' vectors.
 //
-// Inside an item, the wave in lane j of the W lanes takes logical blocks
-// b0 + j, b0 + j + W, ... and keeps a running softmax state (max m, sum l,
+// Inside an item, the wave in lane j of the W lanes takes the item's 16-token
+// positions j, j + W, ... (whole blocks at block size 16, half blocks at 32;
+// the vector-ALU kernel takes whole blocks) and keeps a running softmax state (max m, sum l,
 // weighted sum acc) per query head of the group; the W states are merged
 // through LDS in lane order.  A sequence with one partition writes `out`
 // directly; otherwise the item stores its partition state in the workspace
@@ -809,7 +810,7 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
 struct Desc {
   int s, h, L, b0, nparts, part;
   int wr;           // the wave's lane in the item: (w + round) mod W
-  int nmine;        // the wave's blocks in the item: b0 + wr, b0 + wr + W, ...
+  int nmine;        // the wave's 16-token positions in the item: wr, wr + W, ...
   int npos;         // positions the wave spends on the item: max(nmine, 1)
   bool valid;
 };
@@ -976,8 +977,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     // Rotating the waves' lanes from item to item spreads the extra blocks of
     // items whose size is not a multiple of W evenly over the waves.
     d.wr = (w + r) & (W - 1);
-    d.nmine = nb > d.wr ? (nb - d.wr + W - 1) / W : 0;
-    d.npos = d.nmine > 0 ? d.nmine * kHalves : 1;
+    // Waves take the item's live 16-token positions (half blocks at block
+    // size 32) in turn: position q = wr + k * W is half q % kHalves of block
+    // b0 + q / kHalves.  Dealing whole 32-token blocks to the waves instead
+    // made the block-size-32 kernel 1.1% slower (196.2 against 194.0 us on
+    // the large-batch workload); at block size 16 the two are the same.
+    const int nq = nb > 0 ? (min(d.L, (d.b0 + nb) * BS) - d.b0 * BS + 15) / 16 : 0;
+    d.nmine = nq > d.wr ? (nq - d.wr + W - 1) / W : 0;
+    d.npos = d.nmine > 0 ? d.nmine : 1;
     return d;
   };
 
@@ -1013,10 +1020,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // decode call 4.4% slower (219.5 against 209.8 us on the large-batch
   // workload), the extra cache traffic competing with the tile stream.
   auto load_pos = [&](Tile<D, 16>& t, const Desc& d, int k, bool& has) {
-    const int kk = k / kHalves, half = k - kk * kHalves;
+    const int q = d.wr + k * W;
+    const int kk = q / kHalves, half = q - kk * kHalves;
     int id = 0;
-    if (d.valid && kk < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + d.wr + kk * W];
-    has = d.valid && kk < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
+    if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + kk];
+    has = d.valid && k < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
     const int64_t off = has ? ((int64_t)id * Hkv + d.h) * tile_bytes : 0;
     const uint32_t nb = has ? tile_bytes : 0;
     load_half<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo, half);
@@ -1230,7 +1238,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     }
     load_pos(tn, last ? nxt : cur, last ? 0 : k + 1, hn);
     const int live =
-        hc ? cur.L - (cur.b0 + cur.wr + (k / kHalves) * W) * BS - (k % kHalves) * 16 : 0;
+        hc ? cur.L - cur.b0 * BS - (cur.wr + k * W) * 16 : 0;
     if (r & 1) compute(tc, qb, live);
     else compute(tc, qa, live);
     if (!last) {
