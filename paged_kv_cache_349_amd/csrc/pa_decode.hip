@@ -61,6 +61,7 @@
 // rows (see prefix_items), then the sequences' own blocks as above.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -908,7 +909,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
                                        __HIP_MEMORY_SCOPE_WORKGROUP) < r;
     if (__builtin_amdgcn_readfirstlane(claimer)) {
       const int x = (bid >> 1) & (kClaimPools - 1);
-      if (bid >= a.num_cus) {
+      // Pool x holds workgroups 2x, 2x + 1 (mod 64); its lowest, 2x, is a
+      // first workgroup when 2x < num_cus.  Only then may the others stop
+      // early: a pool without a first workgroup (fewer than 64 CUs, or an
+      // unknown CU count) is emptied by whoever claims from it.
+      if (a.num_cus > 0 && bid >= a.num_cus && 2 * x < a.num_cus) {
         // A workgroup dispatched after its CU's first one streams slower
         // (timestamps: the last workgroups to end were all of these); it
         // leaves a pool's last kLateStop items to the first workgroups, which
@@ -1572,8 +1577,11 @@ void lds_layout_for(int group, int* slots, int* records) {
   *records = nr;
 }
 
-// Compute units of the current device (0 if unknown).
+// Compute units of the current device (0 if unknown).  PA_NUM_CUS_OVERRIDE
+// (read at every call) replaces it, so tests can check the claim pools of a
+// device with fewer CUs, or of one whose count is unknown, on this one.
 int cu_count() {
+  if (const char* o = getenv("PA_NUM_CUS_OVERRIDE")) return atoi(o);
   static std::mutex mu;
   static std::map<int, int> cache;
   int dev = 0;

@@ -319,3 +319,19 @@ def test_many_sequences_past_the_planner_cache():
         _say(f"  partition_tokens={pt} max-abs err {err:.3e}")
         assert err <= TOL["bf16"]
         assert np.all(out[np.asarray(lens) == 0] == 0.0)
+
+
+@pytest.mark.parametrize("cus", ["16", "0", "300"])
+def test_claim_pools_with_other_cu_counts(cus, monkeypatch):
+    """The decode kernel's claim pools stay complete when the device reports
+    fewer CUs than there are pools (so some pools hold no first workgroup), an
+    unknown count, or more CUs than workgroups: every item is still computed."""
+    monkeypatch.setenv("PA_NUM_CUS_OVERRIDE", cus)
+    for cfg in (2, 5):
+        w, _, _, ref = _case(cfg=cfg)
+        _say(f"cus={cus} case {w.name}")
+        out = _run(w).out.cpu().numpy()
+        err = float(np.abs(out - ref).max())
+        _say(f"  max-abs err {err:.3e}")
+        assert np.isfinite(out).all()
+        assert err <= TOL["bf16"]
