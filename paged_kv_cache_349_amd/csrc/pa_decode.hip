@@ -187,6 +187,14 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     nsplit_long = 0;
     npitems = 0;
   }
+  // Group g's bounds and prefix hint, read by thread g (for the first 1024
+  // groups) together with the lengths, in one memory round trip.
+  int reg_lo = 0, reg_hi = 0, reg_pb = 0;
+  if (prefix && tid < a.num_groups) {
+    reg_lo = a.group_starts[tid];
+    reg_hi = a.group_starts[tid + 1];
+    reg_pb = a.prefix_blocks[tid];
+  }
   // One pass over the context lengths (clamped), kept in LDS for the passes
   // below.  S * max_blocks fits in int32 (checked on the host).
   for (int s = tid; s < S; s += 1024) {
@@ -202,8 +210,8 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // read once per `per_item` sequences.  A group of one shares nothing.
   const int per_item = prefix ? (a.prefix_rows / a.group > 0 ? a.prefix_rows / a.group : 1) : 1;
   auto group_range = [&](int g, int& lo, int& hi) {
-    lo = max(a.group_starts[g], 0);
-    hi = min(a.group_starts[g + 1], S);
+    lo = max(g == tid ? reg_lo : a.group_starts[g], 0);
+    hi = min(g == tid ? reg_hi : a.group_starts[g + 1], S);
   };
   int pre_mine = 0;
   if (prefix) {
@@ -213,7 +221,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       if (hi - lo < 2) continue;
       int minL = len_of(lo);
       for (int s = lo + 1; s < hi; ++s) minL = min(minL, len_of(s));
-      const int P = min(a.prefix_blocks[g], minL / block_size);
+      const int P = min(g == tid ? reg_pb : a.prefix_blocks[g], minL / block_size);
       if (P <= 0) continue;
       for (int s = lo; s < hi; ++s) start_c[s] = P;
       pre_mine += (hi - lo + per_item - 1) / per_item * P;
@@ -385,15 +393,17 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 
 // The planner alone, or the planner in workgroup 0 and a slot write in the
 // others (the step's write and plan are independent, so they share a launch).
-__global__ __launch_bounds__(1024) void plan_items(DecodeParams a, int block_size) {
-  plan_body(a, block_size);
+// The block size is a template parameter so that the planner's divisions by
+// it are shifts.
+template <int BS>
+__global__ __launch_bounds__(1024) void plan_items(DecodeParams a) {
+  plan_body(a, BS);
 }
 
-template <typename E>
-__global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, int block_size,
-                                                       WriteArgs w) {
+template <typename E, int BS>
+__global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, WriteArgs w) {
   if (blockIdx.x == 0) {
-    plan_body(a, block_size);
+    plan_body(a, BS);
     return;
   }
   write_elements<E>(w, (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x,
@@ -1654,11 +1664,11 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
     if (wblocks > 4096) wblocks = 4096;   // grid-stride loop covers the rest
     const dim3 grid((unsigned)(1 + wblocks));
     if (write->elem_bytes == 2)
-      hipLaunchKernelGGL(write_and_plan<uint16_t>, grid, dim3(1024), 0, stream, p, BS, *write);
+      hipLaunchKernelGGL((write_and_plan<uint16_t, BS>), grid, dim3(1024), 0, stream, p, *write);
     else
-      hipLaunchKernelGGL(write_and_plan<uint32_t>, grid, dim3(1024), 0, stream, p, BS, *write);
+      hipLaunchKernelGGL((write_and_plan<uint32_t, BS>), grid, dim3(1024), 0, stream, p, *write);
   } else {
-    hipLaunchKernelGGL(plan_items, dim3(1), dim3(1024), 0, stream, p, BS);
+    hipLaunchKernelGGL(plan_items<BS>, dim3(1), dim3(1024), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
