@@ -182,6 +182,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * num_heads / num_kv_heads in [1, 16], kv_dtype F32 or BF16.
  * The reduction order depends only on logical positions, so results are
  * bitwise reproducible and independent of where the blocks sit in the pool.
+ * The environment variable PA_NUM_CUS_OVERRIDE, if set, replaces the device's
+ * CU count in how the kernel shares out its work (a test hook; it changes
+ * which workgroup computes what, never the result).
  */
 int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
