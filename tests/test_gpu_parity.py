@@ -335,3 +335,37 @@ def test_claim_pools_with_other_cu_counts(cus, monkeypatch):
         _say(f"  max-abs err {err:.3e}")
         assert np.isfinite(out).all()
         assert err <= TOL["bf16"]
+
+
+RANDOM_CASES = list(range(24))
+
+
+@pytest.mark.parametrize("seed", RANDOM_CASES)
+def test_random_batches(seed):
+    """Seeded random batches over the compiled shapes: batch sizes 1..48, lengths
+    0..1500 drawn log-uniformly, random group sizes, head dims, block sizes,
+    dtypes and partition sizes, shuffled pools with NaN poison; write and decode
+    against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    S = int(rng.integers(1, 49))
+    lens = [0 if rng.random() < 0.05 else int(np.exp(rng.uniform(0, np.log(1500)))) for _ in range(S)]
+    lens = [max(0, min(l, 1500)) for l in lens]
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    dt = str(rng.choice(["f32", "bf16"]))
+    pt = int(rng.choice([0, bs, 2 * bs, 8 * bs, 64 * bs]))
+    w = _custom(lens, Hkv * G, Hkv, D, bs, dt, seed=seed)
+    _say(f"seed={seed} S={S} Hq={Hkv * G} Hkv={Hkv} D={D} bs={bs} {dt} pt={pt} maxL={max(lens)}")
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, bs)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, bs, dt)
+    from paged_kv_cache_349_amd.device_io import torch_to_np
+    d = _run(w, partition_tokens=pt)
+    assert np.array_equal(_raw(torch_to_np(d.k_cache, dt)), _raw(k_ref))
+    assert np.array_equal(_raw(torch_to_np(d.v_cache, dt)), _raw(v_ref))
+    out = d.out.cpu().numpy()
+    err = float(np.abs(out - ref).max()) if out.size else 0.0
+    _say(f"  max-abs err {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[dt]
