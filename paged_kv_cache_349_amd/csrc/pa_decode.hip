@@ -82,7 +82,7 @@ constexpr int kTailClasses = 256;
 constexpr int kMaxLdsSlots = 2;    // LDS state slots of the matrix-core kernel (power of 2)
 constexpr int kMaxLdsRecords = 16; // LDS output records of the matrix-core kernel
 constexpr int kSpinLimit = 1 << 22; // polls (~0.1 s) before an LDS wait is declared broken
-constexpr int kLateStop = 8;        // items of a claim pool left to the first workgroups
+constexpr int kLateStop = 2;        // items of a claim pool left to the first workgroups
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -927,10 +927,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         // A workgroup dispatched after its CU's first one streams slower
         // (timestamps: the last workgroups to end were all of these); it
         // leaves a pool's last kLateStop items to the first workgroups, which
-        // claim until the pool is empty.  Same host, alternating builds, kernel
-        // with kLateStop 0 / 4 / 8 / 16: gqa 54.0 / 52.2 / 51.5 / 51.5 us,
-        // parallel sampling (shared prefix) 55.6 / 54.2 / 54.5 / 55.0 us,
-        // large batch 189.1 / 189.2 / 189.1 / 189.0 us.
+        // claim until the pool is empty.  Kernel with kLateStop 0 / 2 / 4 / 8,
+        // alternating builds on one host: skewed long context 33.9 / 33.8 /
+        // 35.2 / 36.4 us (uniform items: stopping early idles half the
+        // workgroups at the end), gqa 52.2 / 52.1 / 52.1 / 51.7 us, large
+        // batch and parallel sampling unchanged.  (On another host kLateStop
+        // 8 gave gqa 51.5 against 54.0 us; skewed-long was not measured.)
         int stop = 0;
         if (lane == 0) {
           const int64_t left = (int64_t)total - NG - x;
