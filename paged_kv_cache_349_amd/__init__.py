@@ -128,6 +128,48 @@ def _on_gpu(*ts):
     return dev
 
 
+def _validating(flag) -> bool:
+    return bool(flag) or os.environ.get("PA_VALIDATE", "") not in ("", "0")
+
+
+def check_slots(slots, num_blocks: int, block_size: int) -> None:
+    """Host check of pa_write_kv's device-side preconditions (debugging aid):
+    every non-negative slot is below num_blocks * block_size and no two tokens
+    share a slot.  `slots` is array-like (host)."""
+    import numpy as np
+    s = np.asarray(slots, dtype=np.int64).reshape(-1)
+    live = s[s >= 0]
+    bad = live[live >= int(num_blocks) * int(block_size)]
+    if bad.size:
+        raise ValueError(f"slot {int(bad[0])} is outside the pool of {num_blocks} blocks of {block_size}")
+    uniq, counts = np.unique(live, return_counts=True)
+    if (counts > 1).any():
+        raise ValueError(f"slot {int(uniq[counts > 1][0])} is written by more than one token")
+
+
+def check_tables(block_tables, context_lens, num_blocks: int, block_size: int) -> None:
+    """Host check of pa_decode's device-side preconditions (debugging aid):
+    0 <= L <= max_blocks * block_size and every block id a context reaches
+    (the first ceil(L / block_size) entries of its row) is in [0, num_blocks).
+    Arguments are array-like (host)."""
+    import numpy as np
+    t = np.asarray(block_tables, dtype=np.int64)
+    lens = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    if t.ndim != 2 or t.shape[0] != lens.shape[0]:
+        raise ValueError("block_tables must be [S, max_blocks] with S = len(context_lens)")
+    limit = t.shape[1] * int(block_size)
+    for s_idx, L in enumerate(lens):
+        if L < 0 or L > limit:
+            raise ValueError(f"context_lens[{s_idx}] = {int(L)} is outside [0, {limit}]")
+        nb = -(-int(L) // int(block_size))
+        row = t[s_idx, :nb]
+        bad = np.nonzero((row < 0) | (row >= int(num_blocks)))[0]
+        if bad.size:
+            j = int(bad[0])
+            raise ValueError(f"block_tables[{s_idx}, {j}] = {int(row[j])} is outside the pool of "
+                             f"{num_blocks} blocks (context length {int(L)})")
+
+
 def v_pool_shape(num_blocks, num_kv_heads, head_dim, block_size):
     """Shape of the V pool for a K pool [num_blocks, num_kv_heads, block_size, head_dim]."""
     T = 16 if block_size % 16 == 0 else block_size
@@ -137,8 +179,10 @@ def v_pool_shape(num_blocks, num_kv_heads, head_dim, block_size):
 _V_SHAPE_MSG = "v_cache must be [NB, Hkv, (bs/T)*D, T], T = 16 if 16 divides bs else bs"
 
 
-def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
-    """Copy new tokens' K/V into their slots (raw bits; slot < 0 skipped)."""
+def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None, *, validate=False):
+    """Copy new tokens' K/V into their slots (raw bits; slot < 0 skipped).
+    validate=True (or PA_VALIDATE=1) first checks the slots on the host, which
+    synchronises: for debugging."""
     torch = _torch()
     lib = load_library()
     dev = _on_gpu(k_cache, v_cache, k_new, v_new, slot_mapping)
@@ -150,6 +194,8 @@ def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
     T = slot_mapping.shape[0]
     _need(tuple(k_new.shape) == (T, Hkv, D) and tuple(v_new.shape) == (T, Hkv, D),
           "k_new/v_new must be [T, Hkv, D]")
+    if _validating(validate):
+        check_slots(slot_mapping.cpu().numpy(), NB, bs)
     _check(lib.pa_write_kv(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
                            v_new.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, bs,
                            _dtype_code(k_cache), _stream_handle(dev, stream)))
@@ -232,8 +278,10 @@ def _workspace(dev, stream_handle, nbytes):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None,
-           *, workspace=None, partition_tokens=0, vector_alu=False):
-    """Single-query attention per sequence over the paged KV pool; writes `out`."""
+           *, workspace=None, partition_tokens=0, vector_alu=False, validate=False):
+    """Single-query attention per sequence over the paged KV pool; writes `out`.
+    validate=True (or PA_VALIDATE=1) first checks the tables and lengths on the
+    host, which synchronises: for debugging."""
     torch = _torch()
     lib = load_library()
     dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens)
@@ -248,6 +296,8 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
           block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
     _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
           "context_lens: int32 [S]")
+    if _validating(validate):
+        check_tables(block_tables.cpu().numpy(), context_lens.cpu().numpy(), NB, bs)
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code, partition_tokens)
@@ -265,8 +315,9 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
 
 
 def decode_step(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tables, context_lens,
-                scale, block_size, stream=None, *, workspace=None):
-    """write_kv(...) then decode(...) in one call (the write shares the planner's launch)."""
+                scale, block_size, stream=None, *, workspace=None, validate=False):
+    """write_kv(...) then decode(...) in one call (the write shares the planner's launch).
+    validate=True (or PA_VALIDATE=1) checks slots, tables and lengths on the host first."""
     torch = _torch()
     lib = load_library()
     dev = _on_gpu(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tables,
@@ -286,6 +337,9 @@ def decode_step(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tabl
           block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
     _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
           "context_lens: int32 [S]")
+    if _validating(validate):
+        check_slots(slot_mapping.cpu().numpy(), NB, bs)
+        check_tables(block_tables.cpu().numpy(), context_lens.cpu().numpy(), NB, bs)
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code)
@@ -302,10 +356,11 @@ def decode_step(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tabl
 
 def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, group_starts,
                          prefix_blocks, scale, block_size, stream=None, *, workspace=None,
-                         partition_tokens=0):
+                         partition_tokens=0, validate=False):
     """decode() for a batch whose groups of consecutive sequences share leading blocks.
 
     group_starts: int32 [num_groups + 1] (device), prefix_blocks: int32 [num_groups].
+    validate=True (or PA_VALIDATE=1) checks the tables and lengths on the host first.
     """
     torch = _torch()
     lib = load_library()
@@ -324,6 +379,8 @@ def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, g
     ng = prefix_blocks.shape[0] if prefix_blocks.dim() == 1 else -1
     _need(group_starts.dtype == torch.int32 and prefix_blocks.dtype == torch.int32 and ng >= 0 and
           tuple(group_starts.shape) == (ng + 1,), "group_starts int32 [G + 1], prefix_blocks int32 [G]")
+    if _validating(validate):
+        check_tables(block_tables.cpu().numpy(), context_lens.cpu().numpy(), NB, bs)
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = int(lib.pa_decode_shared_prefix_workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code,

@@ -369,3 +369,28 @@ def test_random_batches(seed):
     _say(f"  max-abs err {err:.3e}")
     assert np.isfinite(out).all()
     assert err <= TOL[dt]
+
+
+def test_validate_option_rejects_before_launch():
+    """validate=True checks tables, lengths and slots on the host: a broken
+    table raises ValueError and nothing runs; good inputs decode as usual."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    w, _, _, ref = _case(cfg=1)
+    d = upload(w)
+    pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping, validate=True)
+    pa.decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(w.scale),
+              w.block_size, validate=True)
+    torch.cuda.synchronize()
+    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL[w.kv_dtype]
+    bad = d.block_tables.clone()
+    s = int(np.argmax(w.context_lens))
+    bad[s, 0] = w.num_blocks + 5
+    with pytest.raises(ValueError, match="outside the pool"):
+        pa.decode(d.out, d.q, d.k_cache, d.v_cache, bad, d.context_lens, float(w.scale),
+                  w.block_size, validate=True)
+    dup = d.slot_mapping.clone()
+    dup[1] = dup[0]
+    with pytest.raises(ValueError, match="more than one token"):
+        pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, dup, validate=True)
