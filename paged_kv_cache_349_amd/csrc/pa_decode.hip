@@ -83,6 +83,7 @@ constexpr int kMaxLdsSlots = 2;    // LDS state slots of the matrix-core kernel 
 constexpr int kMaxLdsRecords = 16; // LDS output records of the matrix-core kernel
 constexpr int kSpinLimit = 1 << 22; // polls (~0.1 s) before an LDS wait is declared broken
 constexpr int kLateStop = 2;        // items of a claim pool left to the first workgroups
+constexpr int kPoolShift = 1;       // workgroup b claims from pool (b >> kPoolShift) % kClaimPools
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -884,7 +885,13 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // and an XCD with slower memory paths still did an eighth of the list
   // (per-workgroup end times: XCD medians 184.5 to 194.0 us); with x =
   // (b / 2) % 32 each pool spans two XCDs: 201.9 vs 203.7 us on one host
-  // (x = (b / 8) % 32, all eight XCDs per pool: 203.0 us).  Letting a
+  // (x = (b / 8) % 32, all eight XCDs per pool: 203.0 us).  On another host,
+  // whose slow XCDs were 2 and 3 (a pair that shared pools under b / 2), all
+  // eight XCDs per pool won by a little (188.2 vs 188.7 us, skewed long
+  // context 33.6 vs 34.0 us) but plain decode of the parallel-sampling batch
+  // lost 13% (158.8 vs 139.7 us): its samples reread their group's shared
+  // blocks, and pools confined to two XCDs keep those rereads in one L2 more
+  // often.  So two XCDs per pool.  Letting a
   // workgroup whose pool is empty claim from other pools cost more than it
   // saved (a scan of the pools' counters before a workgroup may end: large
   // batch +1 us, small batches +2 to +3 us).  The first wave to need round
@@ -918,12 +925,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
       claimer = __hip_atomic_fetch_max(&s_claim_busy[slot], r, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP) < r;
     if (__builtin_amdgcn_readfirstlane(claimer)) {
-      const int x = (bid >> 1) & (kClaimPools - 1);
-      // Pool x holds workgroups 2x, 2x + 1 (mod 64); its lowest, 2x, is a
+      const int x = (bid >> kPoolShift) & (kClaimPools - 1);
+      // Pool x holds workgroups 2x and 2x + 1 (mod 64); its lowest, 2x, is a
       // first workgroup when 2x < num_cus.  Only then may the others stop
       // early: a pool without a first workgroup (fewer than 64 CUs, or an
       // unknown CU count) is emptied by whoever claims from it.
-      if (a.num_cus > 0 && bid >= a.num_cus && 2 * x < a.num_cus) {
+      if (a.num_cus > 0 && bid >= a.num_cus && (x << kPoolShift) < a.num_cus) {
         // A workgroup dispatched after its CU's first one streams slower
         // (timestamps: the last workgroups to end were all of these); it
         // leaves a pool's last kLateStop items to the first workgroups, which
