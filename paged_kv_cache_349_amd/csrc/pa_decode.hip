@@ -1429,7 +1429,7 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 // reproducible.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = 64 * kMergeWaves;
-constexpr int kMergeBatch = 16;
+constexpr int kMergeBatch = 32;
 constexpr int kMergeHeld = 2;
 constexpr int kMergeGrid = 256;
 static_assert(kMergeShort <= kMergeBatch, "a short unit's partitions are loaded in one batch");
