@@ -32,11 +32,11 @@
 //
 // Inside an item, the wave in lane j of the W lanes takes the item's 16-token
 // positions j, j + W, ... (whole blocks at block size 16, half blocks at 32;
-// the vector-ALU kernel takes whole blocks) and keeps a running softmax state (max m, sum l,
-// weighted sum acc) per query head of the group; the W states are merged
-// through LDS in lane order.  A sequence with one partition writes `out`
-// directly; otherwise the item stores its partition state in the workspace
-// for merge_splits.
+// the vector-ALU kernel takes whole blocks) and keeps a running softmax state
+// (max m, sum l, weighted sum acc) per query head of the group; the W states
+// are merged through LDS in lane order.  A sequence with one partition writes
+// `out` directly; otherwise the item stores its partition state in the
+// workspace for merge_splits.
 //
 // Matrix-core kernel (bf16).  For each 16-token sub-block:
 //   S^T[16 tokens x 16 heads] = K[16 x D] * Q^T[D x 16]      (v_mfma_f32_16x16x32_bf16)
@@ -1419,8 +1419,9 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 //   once and merges them alone, with no barrier.  Unit u goes to workgroup
 //   u % grid, row (u / grid) % R of its R = threads / C rows of C columns:
 //   units spread over all workgroups before any takes a second one.
-//   Long units: one workgroup per unit, the last workgroups first.  Wave g % kMergeWaves finds M and
-//   lambda of head g over lane-strided partitions; rows of threads take
+//   Long units: one workgroup per unit, the last workgroups first.  Wave
+//   g % kMergeWaves finds M and lambda of head g over lane-strided
+//   partitions; rows of threads take
 //   contiguous runs of partitions of one column for the weighted sum, whose
 //   terms do not depend on one another, and the rows' partial sums are added
 //   in row order.  A unit's first loads (kMergeBatch partitions per row,
