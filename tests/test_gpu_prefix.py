@@ -166,3 +166,47 @@ def test_rejects_fp32_and_bad_arguments():
         pa.decode_shared_prefix(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
                                 _i32([0, 4]), _i32([1]), float(w.scale), w.block_size)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_random_groupings(seed):
+    """Seeded random batches of groups: 1..5 groups of 1..12 consecutive
+    sequences sharing 1..10 leading blocks, singletons between them, private
+    tails of 1..301 tokens (a member's decode-time context may end inside the
+    prefix), hints equal to or one below the shared count, random head shapes,
+    block sizes and partition sizes; against the oracle, and bitwise
+    reproducible."""
+    rng = np.random.default_rng(2000 + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    prefix = int(rng.integers(1, 11))
+    lens, dec_lens, groups, starts, hints = [], [], [], [0], []
+    for _ in range(int(rng.integers(1, 6))):
+        if rng.random() < 0.5:                      # a singleton before the group
+            lens.append(int(rng.integers(1, 400)))
+            dec_lens.append(lens[-1])
+            starts.append(len(lens))
+            hints.append(int(rng.integers(0, 4)))
+        n = int(rng.integers(1, 13))
+        first = len(lens)
+        for _ in range(n):
+            lens.append(prefix * bs + int(rng.integers(1, 302)))
+            # a member whose context (at decode time) ends inside the prefix
+            dec_lens.append(int(rng.integers(1, prefix * bs + 1)) if rng.random() < 0.1
+                            else lens[-1])
+        groups.append(list(range(first, first + n)))
+        starts.append(len(lens))
+        hints.append(max(0, prefix - int(rng.integers(0, 2))))
+    pt = int(rng.choice([0, bs, 4 * bs]))
+    w = _custom(lens, groups, prefix, Hkv * G, Hkv, D, bs, seed=seed)
+    _say(f"seed={seed} S={len(lens)} groups={len(groups)} prefix={prefix} Hq={Hkv * G} "
+         f"Hkv={Hkv} D={D} bs={bs} pt={pt}")
+    dl = np.asarray(dec_lens, np.int32)
+    out, _ = _prefix_run(w, starts, hints, lens=dl, partition_tokens=pt)
+    ref = _oracle(w, dl)
+    err = float(np.abs(out - ref).max())
+    _say(f"  max-abs err {err:.2e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL
