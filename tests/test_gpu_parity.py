@@ -394,3 +394,36 @@ def test_validate_option_rejects_before_launch():
     dup[1] = dup[0]
     with pytest.raises(ValueError, match="more than one token"):
         pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, dup, validate=True)
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_decode_step_random_batches(seed):
+    """decode_step on seeded random batches (as test_random_batches) equals
+    write_kv then decode bit for bit, and the oracle within the bar."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    rng = np.random.default_rng(3000 + seed)
+    S = int(rng.integers(1, 49))
+    lens = [int(np.exp(rng.uniform(0, np.log(3000)))) for _ in range(S)]
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    dt = str(rng.choice(["f32", "bf16"]))
+    w = _custom(lens, Hkv * G, Hkv, D, bs, dt, seed=seed)
+    _say(f"seed={seed} S={S} Hq={Hkv * G} Hkv={Hkv} D={D} bs={bs} {dt}")
+    a, b = upload(w), upload(w)
+    pa.write_kv(a.k_cache, a.v_cache, a.k_new, a.v_new, a.slot_mapping)
+    pa.decode(a.out, a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, float(w.scale),
+              bs)
+    pa.decode_step(b.k_cache, b.v_cache, b.k_new, b.v_new, b.slot_mapping, b.out, b.q,
+                   b.block_tables, b.context_lens, float(w.scale), bs)
+    torch.cuda.synchronize()
+    _assert_no_abort()
+    iv = (lambda x: x.view(torch.int16)) if dt == "bf16" else (lambda x: x.view(torch.int32))
+    assert torch.equal(iv(a.k_cache), iv(b.k_cache)) and torch.equal(iv(a.v_cache), iv(b.v_cache))
+    assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, bs)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, bs, dt)
+    assert float(np.abs(b.out.cpu().numpy() - ref).max()) <= TOL[dt]
