@@ -57,6 +57,28 @@ def _sdpa(qs, K, V, scale):
     return o[0, :, 0, :].numpy()
 
 
+def _torch_bf16_to_f64(bits):
+    """bf16 bit patterns -> float64 through torch's own bfloat16 type (not the oracle's code)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _bf16_from_fields(bits):
+    """Value of one bf16 pattern from the format's definition, as an mpmath number:
+    1 sign bit, 8 exponent bits (bias 127), 7 fraction bits; exponent 0 holds
+    zero and the subnormals (fraction * 2^-133), exponent 255 infinities and NaNs."""
+    import mpmath
+    bits = int(bits)
+    sign = -1 if bits >> 15 else 1
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return mpmath.nan if f else sign * mpmath.inf
+    if e == 0:
+        return sign * mpmath.mpf(f) * mpmath.mpf(2) ** -133
+    return sign * (1 + mpmath.mpf(f) / 128) * mpmath.mpf(2) ** (e - 127)
+
+
 # ---------------------------------------------------------------------------
 # pin functions (each returns the max deviation or raises AssertionError)
 # ---------------------------------------------------------------------------
@@ -87,6 +109,86 @@ def pin_library_routine(decode, seed=0):
             worst = max(worst, float(np.abs(out[s] - ref).max()))
     assert worst < 1e-12, worst
     return worst
+
+
+def pin_library_routine_bf16(decode, seed=10):
+    """P1 + P8 on bf16 KV: the oracle's bf16 path == torch SDPA (fp64) on values
+    widened by torch's bfloat16 type.
+
+    Block sizes 4, 16, 32 and 48 (two and three 16-token V sub-tiles for the
+    last two), GQA by head expansion, ragged lengths, shuffled tables.
+    """
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (Hq, Hkv, D, bs, lens) in [(4, 4, 16, 16, [1, 17, 40]),
+                                   (8, 2, 8, 4, [3, 9, 30]),
+                                   (8, 1, 32, 32, [70, 33, 1]),
+                                   (4, 2, 8, 48, [100, 47, 49])]:
+        lk, lv, q, kc, vc, tables, L = _random_paged(rng, lens, Hq, Hkv, D, bs, dtype="bf16")
+        sc = np.float32(1.0 / math.sqrt(D))
+        out = decode(q, kc, vc, tables, L, sc, bs, "bf16")
+        G = Hq // Hkv
+        for s in range(len(lens)):
+            K = np.repeat(_torch_bf16_to_f64(lk[s]), G, axis=0)
+            V = np.repeat(_torch_bf16_to_f64(lv[s]), G, axis=0)
+            ref = _sdpa(_torch_bf16_to_f64(q[s]), K, V, float(sc))
+            worst = max(worst, float(np.abs(out[s] - ref).max()))
+    assert worst < 1e-12, worst
+    return worst
+
+
+def pin_brute_force_bf16(decode, cases=12, seed=11):
+    """P7 on bf16 KV: 50-digit scalar loops over values decoded from the bf16
+    format's fields (sign, exponent, fraction), at block sizes 16 and 32."""
+    import mpmath
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for c in range(cases):
+        bs = [16, 32][c % 2]
+        Hkv = 1 + c % 2
+        G = 1 + (c // 2) % 3
+        D = 1 + int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(1, 70, size=1 + c % 2)]
+        lk, lv, q, kc, vc, tables, L = _random_paged(rng, lens, Hkv * G, Hkv, D, bs, dtype="bf16")
+        sc = np.float32(rng.uniform(0.1, 1.0))
+        out = decode(q, kc, vc, tables, L, sc, bs, "bf16")
+        scm = mpmath.mpf(float(sc))
+        for s, Ls in enumerate(lens):
+            for h in range(Hkv * G):
+                kv = h // G
+                qv = [_bf16_from_fields(q[s, h, d]) for d in range(D)]
+                x = [scm * mpmath.fsum(qv[d] * _bf16_from_fields(lk[s][kv, t, d]) for d in range(D))
+                     for t in range(Ls)]
+                mx = max(x)
+                w = [mpmath.exp(xi - mx) for xi in x]
+                den = mpmath.fsum(w)
+                for d in range(D):
+                    num = mpmath.fsum(w[t] * _bf16_from_fields(lv[s][kv, t, d]) for t in range(Ls))
+                    worst = max(worst, abs(float(num / den) - out[s, h, d]))
+    assert worst < 1e-13, worst
+    return worst
+
+
+def pin_widen_bf16(widen):
+    """The oracle's bf16 widening: every one of the 65536 bit patterns against
+    torch's bfloat16 -> float64 conversion (NaNs as NaNs), and a table of
+    patterns against the format's definition (zeros, subnormals, the smallest
+    and largest normals, infinities)."""
+    import mpmath
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):      # signalling NaN patterns
+        got = widen(bits, "bf16")
+    ref = _torch_bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    table = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x4049, 0x3E00,
+             0x7F7F, 0xFF7F, 0x7F80, 0xFF80]
+    for b in table:
+        v = widen(np.array([b], np.uint16), "bf16")[0]
+        assert mpmath.mpf(float(v)) == _bf16_from_fields(b), hex(b)
+        assert math.copysign(1.0, float(v)) == (-1.0 if b >> 15 else 1.0), hex(b)
 
 
 def pin_brute_force(decode, cases=20, seed=1):
@@ -199,21 +301,56 @@ def pin_split_merge(seed=5):
 
 
 def pin_write_readback(write_kv, seed=6):
-    """P10: each new token's bits land in its slot; every other slot is unchanged."""
-    for i, dt_poison in [(1, "nan"), (2, "finite")]:
-        w = wl.make_config(i, seed=seed, poison=dt_poison, num_seqs=6 if i == 2 else None)
+    """P10: each new token's bits land in its slot; every other element of the
+    pool is unchanged.
+
+    The expected pool is built element by element from the layout as the C
+    header documents it (token o, feature d of block b: K at [b, h, o, d], V at
+    [b, h, (o // T) * D + d, o % T] with T = 16 when 16 divides the block
+    size), at block sizes 16 and 32, with NaN and finite poison.
+    """
+    for i, poison, bs, ns in [(1, "nan", None, None), (2, "finite", None, 6),
+                              (5, "nan", 32, 12), (5, "finite", 32, 7)]:
+        w = wl.make_config(i, seed=seed, poison=poison, block_size=bs, num_seqs=ns)
         k2, v2 = write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, w.block_size)
         raw = (lambda a: a.view(np.uint32)) if w.kv_dtype == "f32" else (lambda a: a)
-        changed_k = np.ones(w.k_cache.shape[:1] + w.k_cache.shape[2:3], dtype=bool) & False
+        exp_k, exp_v = raw(w.k_cache).copy(), raw(w.v_cache).copy()
+        T = 16 if w.block_size % 16 == 0 else w.block_size
+        D = w.head_dim
         for t, slot in enumerate(w.slot_mapping):
             b, o = divmod(int(slot), w.block_size)
-            assert np.array_equal(raw(k2)[b, :, o, :], raw(w.k_new)[t])
-            assert np.array_equal(raw(v2)[b, :, :, o], raw(w.v_new)[t])
-            changed_k[b, o] = True
-        keep = ~changed_k
-        kb, ko = np.nonzero(keep)
-        assert np.array_equal(raw(k2)[kb, :, ko, :], raw(w.k_cache)[kb, :, ko, :])
-        assert np.array_equal(raw(v2)[kb, :, :, ko], raw(w.v_cache)[kb, :, :, ko])
+            for h in range(w.num_kv_heads):
+                for d in range(D):
+                    exp_k[b, h, o, d] = raw(w.k_new)[t, h, d]
+                    exp_v[b, h, (o // T) * D + d, o % T] = raw(w.v_new)[t, h, d]
+        assert np.array_equal(raw(k2), exp_k)
+        assert np.array_equal(raw(v2), exp_v)
+
+
+def pin_write_matches_packing(write_kv, seed=12):
+    """P10 through the input generator's independently written placement
+    (workloads.pack_logical): writing each sequence's last token into a pool
+    that holds the others gives, bit for bit, the pool packed with every token.
+    Block sizes 4, 16, 32 and 48 (one, two and three 16-token V sub-tiles),
+    tokens at every offset class, fp32 and bf16."""
+    rng = np.random.default_rng(seed)
+    for (Hkv, D, bs, lens, dt) in [(2, 8, 4, [3, 9, 30], "f32"),
+                                   (2, 16, 16, [1, 16, 17, 40], "bf16"),
+                                   (3, 8, 32, [32, 17, 33, 64, 50, 2], "bf16"),
+                                   (1, 4, 48, [48, 47, 100, 17, 33, 20], "f32")]:
+        lk, lv, q, kc, vc, tables, L = _random_paged(rng, lens, Hkv, Hkv, D, bs, dtype=dt)
+        fill = np.float32(np.nan) if dt == "f32" else np.uint16(0x7FC0)
+        short_k = [x[:, :-1] for x in lk]
+        short_v = [x[:, :-1] for x in lv]
+        kc0, vc0 = wl.pack_logical(short_k, short_v, tables, kc.shape[0], bs, fill)
+        slots = np.array([int(tables[s, (n - 1) // bs]) * bs + (n - 1) % bs
+                          for s, n in enumerate(lens)], np.int32)
+        k_new = np.stack([x[:, -1] for x in lk])
+        v_new = np.stack([x[:, -1] for x in lv])
+        k2, v2 = write_kv(kc0, vc0, k_new, v_new, slots, bs)
+        raw = (lambda a: a.view(np.uint32)) if dt == "f32" else (lambda a: a)
+        assert np.array_equal(raw(k2), raw(kc))
+        assert np.array_equal(raw(v2), raw(vc))
 
 
 def _read_golden():
@@ -292,6 +429,22 @@ def test_oracle_brute_force_mpmath():
     pin_brute_force(oracle.decode)
 
 
+def test_oracle_bf16_matches_sdpa():
+    pin_library_routine_bf16(oracle.decode)
+
+
+def test_oracle_bf16_brute_force_mpmath():
+    pin_brute_force_bf16(oracle.decode)
+
+
+def test_oracle_bf16_widening():
+    pin_widen_bf16(oracle.widen)
+
+
+def test_oracle_write_matches_packing():
+    pin_write_matches_packing(oracle.write_kv)
+
+
 def test_oracle_shuffle_invariance():
     pin_shuffle_invariance(oracle.decode)
 
@@ -331,13 +484,32 @@ def test_oracle_zero_length_sequence():
 # planted mistakes: each broken copy of the oracle must fail at least one pin
 # ---------------------------------------------------------------------------
 
+def _mutant_widen(kind):
+    def widen(x, kv_dtype):
+        with np.errstate(invalid="ignore"):
+            return _widen(x, kv_dtype)
+
+    def _widen(x, kv_dtype):
+        if kv_dtype == "bf16" and kind == "bf16_as_fp16":      # bits read as IEEE half
+            return x.view(np.float16).astype(np.float64)
+        if kv_dtype == "bf16" and kind == "bf16_shift15":      # fraction misplaced by one bit
+            return (x.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        if kv_dtype == "bf16" and kind == "bf16_truncated":    # low fraction bit dropped
+            return ((x & np.uint16(0xFFFE)).astype(np.uint32) << np.uint32(16)).view(
+                np.float32).astype(np.float64)
+        return oracle.widen(x, kv_dtype)
+    return widen
+
+
 def _mutant_decode(kind):
+    wid = _mutant_widen(kind)
+
     def decode(q, k_cache, v_cache, block_tables, context_lens, scale, block_size, kv_dtype):
         S, Hq, D = q.shape
         Hkv = k_cache.shape[1]
         G = Hq // Hkv
         sc = float(np.float32(scale))
-        qd = oracle.widen(q, kv_dtype)
+        qd = wid(q, kv_dtype)
         out = np.zeros((S, Hq, D))
         for s in range(S):
             L = int(context_lens[s])
@@ -349,18 +521,18 @@ def _mutant_decode(kind):
             if kind == "offset_from_block":
                 bl = block_tables[s][pos % max(1, (L + block_size - 1) // block_size)].astype(np.int64)
             off = pos % block_size
-            K = oracle.widen(k_cache[bl, :, off, :], kv_dtype).transpose(1, 0, 2)
+            K = wid(k_cache[bl, :, off, :], kv_dtype).transpose(1, 0, 2)
             if kind == "v_whole_block_tile":             # V feature-major over the whole block
                 whole = v_cache.reshape(v_cache.shape[0], Hkv, D, block_size)
-                V = oracle.widen(whole[bl, :, :, off], kv_dtype)
+                V = wid(whole[bl, :, :, off], kv_dtype)
                 V = V.transpose(1, 0, 2)
             elif kind == "v_as_k_layout":
-                V = oracle.widen(v_cache.reshape(k_cache.shape)[bl, :, off, :], kv_dtype)
+                V = wid(v_cache.reshape(k_cache.shape)[bl, :, off, :], kv_dtype)
                 V = V.transpose(1, 0, 2)
             else:
                 T = v_cache.shape[3]           # feature-major sub-tiles of T tokens
                 rows = (off // T)[:, None] * D + np.arange(D)[None, :]
-                V = oracle.widen(v_cache[bl[:, None], :, rows, (off % T)[:, None]], kv_dtype)
+                V = wid(v_cache[bl[:, None], :, rows, (off % T)[:, None]], kv_dtype)
                 V = V.transpose(2, 0, 1)
             for h in range(Hq):
                 kv = (h % Hkv) if kind == "gqa_modulo" else h // G
@@ -376,12 +548,15 @@ def _mutant_decode(kind):
 
 
 def _fails_some_pin(dec):
-    pins = [pin_library_routine, pin_brute_force, pin_shuffle_invariance, pin_closed_forms,
-            pin_shared_blocks, lambda d: pin_pages_mapping(d, oracle.write_kv)]
+    pins = [pin_library_routine, pin_brute_force, pin_library_routine_bf16, pin_brute_force_bf16,
+            pin_shuffle_invariance, pin_closed_forms, pin_shared_blocks,
+            lambda d: pin_pages_mapping(d, oracle.write_kv)]
     for pin in pins:
         try:
             if pin is pin_brute_force:
                 pin(dec, cases=6)
+            elif pin is pin_brute_force_bf16:
+                pin(dec, cases=4)
             else:
                 pin(dec)
         except (AssertionError, IndexError, ValueError):
@@ -391,9 +566,16 @@ def _fails_some_pin(dec):
 
 @pytest.mark.parametrize("kind", ["drop_last_token", "offset_from_block", "v_as_k_layout",
                                   "v_whole_block_tile",
-                                  "gqa_modulo", "no_scale", "neg_scores", "no_normalise"])
+                                  "gqa_modulo", "no_scale", "neg_scores", "no_normalise",
+                                  "bf16_as_fp16", "bf16_shift15", "bf16_truncated"])
 def test_planted_mistake_is_caught(kind):
     assert _fails_some_pin(_mutant_decode(kind)), kind
+
+
+@pytest.mark.parametrize("kind", ["bf16_as_fp16", "bf16_shift15", "bf16_truncated"])
+def test_planted_widen_mistake_is_caught(kind):
+    with pytest.raises(AssertionError):
+        pin_widen_bf16(_mutant_widen(kind))
 
 
 def test_unmutated_copy_passes_pins():
@@ -403,6 +585,8 @@ def test_unmutated_copy_passes_pins():
 def _mutant_write(kind):
     def write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, block_size):
         k, v = k_cache.copy(), v_cache.copy()
+        D = k.shape[3]
+        T = v.shape[3]
         for t, slot in enumerate(slot_mapping):
             if slot < 0:
                 continue
@@ -410,15 +594,30 @@ def _mutant_write(kind):
             if kind == "swap_block_offset":
                 b, o = o % k.shape[0], b % block_size
             k[b, :, o, :] = k_new[t]
+            row = (o // T) * D
+            if kind == "v_subtile0":                 # every token into the first sub-tile
+                row = 0
             if kind == "v_untransposed":
                 v.reshape(k.shape)[b, :, o, :] = v_new[t]
             else:
-                v[b, :, :, o] = v_new[t]
+                v[b, :, row:row + D, o % T] = v_new[t]
         return k, v
     return write_kv
 
 
-@pytest.mark.parametrize("kind", ["swap_block_offset", "v_untransposed"])
+def _write_fails_some_pin(write):
+    for pin in (pin_write_readback, pin_write_matches_packing):
+        try:
+            pin(write)
+        except (AssertionError, IndexError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["swap_block_offset", "v_untransposed", "v_subtile0"])
 def test_planted_write_mistake_is_caught(kind):
-    with pytest.raises(AssertionError):
-        pin_write_readback(_mutant_write(kind))
+    assert _write_fails_some_pin(_mutant_write(kind)), kind
+
+
+def test_unmutated_write_copy_passes_pins():
+    assert not _write_fails_some_pin(_mutant_write("none"))

@@ -27,6 +27,19 @@ def test_bf16_rounding_nearest_even():
     assert np.all(np.abs(back - x) <= np.abs(x) * 2 ** -8)
 
 
+def test_bf16_rounding_matches_torch():
+    """The generator's rounding equals torch's fp32 -> bfloat16 conversion (round to
+    nearest, ties to even) on random draws and on exact ties between neighbours."""
+    import torch
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0)
+    u = rng.integers(0, 1 << 16, size=4096, dtype=np.uint32) << np.uint32(16)
+    ties = ((u & np.uint32(0x7F7F0000)) | np.uint32(0x8000)).view(np.float32)   # halfway points
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1e-40, -1e-40])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wl.f32_to_bf16_bits(x), ref)
+
+
 def test_config1_shape_and_lengths():
     w = wl.make_config(1)
     assert w.kv_dtype == "f32" and w.num_blocks == 48
