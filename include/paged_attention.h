@@ -183,8 +183,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * The reduction order depends only on logical positions, so results are
  * bitwise reproducible and independent of where the blocks sit in the pool.
  * The environment variable PA_NUM_CUS_OVERRIDE, if set, replaces the device's
- * CU count in how the kernel shares out its work (a test hook; it changes
- * which workgroup computes what, never the result).
+ * CU count in how the kernel shares out its work, and PA_DECODE_GRID_OVERRIDE,
+ * if set to a positive number below the default, the number of workgroups of
+ * the attention launch (test hooks; they change which workgroup computes
+ * what, never the result).
+ * After the call, pa_decode_check reports whether its kernels completed.
  */
 int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -227,7 +230,10 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_heads, int32_t
  *
  *   group_starts   [num_groups + 1] int32, device: group g is sequences
  *                  group_starts[g] .. group_starts[g+1]-1 (non-decreasing;
- *                  sequences outside every group are decoded as usual)
+ *                  sequences outside every group are decoded as usual; a
+ *                  list that is not non-decreasing is ignored: the batch is
+ *                  then decoded without shared prefixes, which gives the
+ *                  same result; values are clamped to [0, num_seqs])
  *   prefix_blocks  [num_groups] int32, device: leading table entries that
  *                  every sequence of group g has in common.  Only whole
  *                  blocks inside every member's context are treated as
@@ -255,6 +261,26 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_hea
                                                int32_t num_kv_heads, int32_t head_dim,
                                                int32_t max_blocks_per_seq, int32_t block_size,
                                                int32_t kv_dtype, int32_t partition_tokens);
+
+/*
+ * Completion check of the last decode call that used `workspace` (pa_decode,
+ * pa_decode_ex, pa_decode_step or pa_decode_shared_prefix).  The attention
+ * kernel's waves hand work to one another through the workgroup's shared
+ * memory; each such wait is bounded, and a wait that does not end (a broken
+ * invariant, never expected) is given up so that the kernel still ends:
+ * that call's output is then incomplete.  The kernel records it in the int32
+ * word at byte offset 80 of the workspace (the planner clears it at the start
+ * of every call).  This call enqueues on `stream` a copy of that word into
+ * *flag: 0 = every wait ended, 1 = the output of that call is incomplete.
+ *   workspace   the workspace the decode call used (device, 256-byte aligned,
+ *               workspace_bytes >= 4224, as any decode workspace is)
+ *   flag        one int32, device memory or pinned host memory (4-byte
+ *               aligned); valid once `stream` has reached this point
+ * Errors (reported before anything is enqueued): a null pointer or a
+ * misaligned flag is PA_ERR_INVALID_ARG; a misaligned or too small workspace
+ * is PA_ERR_WORKSPACE.  The call allocates nothing and does not synchronise.
+ */
+int pa_decode_check(const void* workspace, size_t workspace_bytes, int32_t* flag, void* stream);
 
 /* Tokens per partition that pa_decode picks for these shapes (0 if invalid). */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": (ctypes.c_int, [_vp] * 8 + [_c_int, ctypes.c_float] + [_c_int] * 8 +
                                 [_vp, ctypes.c_size_t, _c_int, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [_c_int] * 8),
+    "pa_decode_check": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "pa_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "pa_probe_read_tiles": (ctypes.c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _vp,
                                            _vp]),
@@ -108,11 +109,14 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported KV dtype {t.dtype}")
 
 
-def _stream_handle(device, stream):
+def _stream_of(device, stream):
+    """The torch stream a call runs on: `stream`, or the device's current stream."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _stream_handle(device, stream):
+    return _stream_of(device, stream).cuda_stream
 
 
 def _need(cond: bool, msg: str):
@@ -168,6 +172,21 @@ def check_tables(block_tables, context_lens, num_blocks: int, block_size: int) -
             j = int(bad[0])
             raise ValueError(f"block_tables[{s_idx}, {j}] = {int(row[j])} is outside the pool of "
                              f"{num_blocks} blocks (context length {int(L)})")
+
+
+def check_groups(group_starts, num_seqs: int) -> None:
+    """Host check of pa_decode_shared_prefix's group list (debugging aid):
+    group_starts is non-decreasing and inside [0, num_seqs].  (The kernels
+    ignore a list that is not non-decreasing and decode the batch plainly.)"""
+    import numpy as np
+    g = np.asarray(group_starts, dtype=np.int64).reshape(-1)
+    if g.size and (g.min() < 0 or g.max() > int(num_seqs)):
+        raise ValueError(f"group_starts must lie in [0, {num_seqs}]")
+    drop = np.nonzero(np.diff(g) < 0)[0]
+    if drop.size:
+        i = int(drop[0])
+        raise ValueError(f"group_starts[{i + 1}] = {int(g[i + 1])} < group_starts[{i}] = {int(g[i])}: "
+                         "groups must be ordered")
 
 
 def v_pool_shape(num_blocks, num_kv_heads, head_dim, block_size):
@@ -267,14 +286,39 @@ def workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_blocks, blo
 _workspaces = {}
 
 
-def _workspace(dev, stream_handle, nbytes):
+def _workspace(dev, stream, nbytes):
+    """The binding's workspace for kernels launched on torch stream `stream`.
+
+    It is allocated on that stream, so when a larger one replaces it the
+    caching allocator gives the old block only to later work on the same
+    stream, which runs after the kernels that may still use it."""
     torch = _torch()
-    key = (dev.index, stream_handle)
+    key = (dev.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
+
+
+def decode_check(workspace=None, stream=None, device=None) -> int:
+    """Abort word of the last decode call that used `workspace` (by default the
+    binding's own workspace for `device` and `stream`): 0 if that call's kernels
+    completed every wait, 1 if one gave up a wait (its output is then
+    incomplete).  Enqueues the read on the stream and synchronises it."""
+    torch = _torch()
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    st = _stream_of(dev, stream)
+    if workspace is None:
+        workspace = _workspaces.get((dev.index, st.cuda_stream))
+        _need(workspace is not None, "no decode has run on this device and stream")
+    flag = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    _check(lib.pa_decode_check(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               flag.data_ptr(), st.cuda_stream))
+    st.synchronize()
+    return int(flag.item())
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None,
@@ -301,9 +345,10 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code, partition_tokens)
-    sh = _stream_handle(dev, stream)
+    st = _stream_of(dev, stream)
+    sh = st.cuda_stream
     if workspace is None:
-        workspace = _workspace(dev, sh, need)
+        workspace = _workspace(dev, st, need)
     ws_ptr = workspace.data_ptr()
     ws_len = workspace.numel() * workspace.element_size()
     flags = PA_FLAG_VECTOR_ALU if vector_alu else 0
@@ -343,9 +388,10 @@ def decode_step(k_cache, v_cache, k_new, v_new, slot_mapping, out, q, block_tabl
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code)
-    sh = _stream_handle(dev, stream)
+    st = _stream_of(dev, stream)
+    sh = st.cuda_stream
     if workspace is None:
-        workspace = _workspace(dev, sh, need)
+        workspace = _workspace(dev, st, need)
     _check(lib.pa_decode_step(
         k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
         slot_mapping.data_ptr(), T, out.data_ptr(), q.data_ptr(), block_tables.data_ptr(),
@@ -381,13 +427,15 @@ def decode_shared_prefix(out, q, k_cache, v_cache, block_tables, context_lens, g
           tuple(group_starts.shape) == (ng + 1,), "group_starts int32 [G + 1], prefix_blocks int32 [G]")
     if _validating(validate):
         check_tables(block_tables.cpu().numpy(), context_lens.cpu().numpy(), NB, bs)
+        check_groups(group_starts.cpu().numpy(), S)
     code = _dtype_code(k_cache)
     max_blocks = block_tables.shape[1]
     need = int(lib.pa_decode_shared_prefix_workspace_bytes(S, Hq, Hkv, D, max_blocks, bs, code,
                                                            partition_tokens))
-    sh = _stream_handle(dev, stream)
+    st = _stream_of(dev, stream)
+    sh = st.cuda_stream
     if workspace is None:
-        workspace = _workspace(dev, sh, need)
+        workspace = _workspace(dev, st, need)
     _check(lib.pa_decode_shared_prefix(
         out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         block_tables.data_ptr(), context_lens.data_ptr(), group_starts.data_ptr(),
@@ -427,5 +475,7 @@ def kernel_timing_end():
     return ms.value, n.value
 
 
-__all__ = ["v_pool_shape", "write_kv", "decode", "decode_step", "decode_shared_prefix", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
-           "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end"]
+__all__ = ["v_pool_shape", "write_kv", "decode", "decode_step", "decode_shared_prefix",
+           "decode_check", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+           "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end",
+           "check_slots", "check_tables", "check_groups"]

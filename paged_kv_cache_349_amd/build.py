@@ -30,6 +30,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HOST = ["-O3", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-Wall",
+        "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def _hipcc() -> str:
@@ -41,8 +44,10 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [_hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    # Device sources as HIP; the host-only C++ sources (C ABI, block manager)
+    # as plain C++.
+    flags = [*COMMON, "-x", "hip"] if src.endswith(".hip") else [*HOST, "-x", "c++"]
+    cmd = [_hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -14,7 +14,6 @@
 #include <vector>
 
 #include "pa_internal.h"
-#include "pa_write_body.h"
 
 namespace {
 thread_local char g_last_error[512];
@@ -234,9 +233,14 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
   p.prefix_rows = 0;   // set by the launcher
   p.ws_pitems = prefix ? (int4*)(ws + lay.pitems_off) : nullptr;
   const auto ev = next_timing_events();
-  hipError_t e = pa::launch_decode(p, (pa::KvType)kv_dtype, head_dim, block_size,
-                                   (flags & PA_FLAG_VECTOR_ALU) != 0, (hipStream_t)stream,
-                                   ev.first, ev.second, write);
+  hipError_t e = pa::launch_decode(p, sizeof(pa::DecodeParams), (pa::KvType)kv_dtype, head_dim,
+                                   block_size, (flags & PA_FLAG_VECTOR_ALU) != 0,
+                                   (hipStream_t)stream, ev.first, ev.second, write);
+  if (e == hipErrorInvalidImage)
+    return fail(PA_ERR_LAUNCH,
+                "decode launch: the library's objects disagree on the launch-parameter layout "
+                "(%zu bytes here); rebuild every object",
+                sizeof(pa::DecodeParams));
   if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -440,6 +444,21 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
   return pa_decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                       num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int pa_decode_check(const void* workspace, size_t workspace_bytes, int32_t* flag, void* stream) {
+  if (!workspace || !flag) return fail(PA_ERR_INVALID_ARG, "null workspace or flag pointer");
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(PA_ERR_WORKSPACE, "workspace at %p must be 256-byte aligned", workspace);
+  if (workspace_bytes < (size_t)pa::kCtrlSize * sizeof(int32_t))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than any decode workspace",
+                workspace_bytes);
+  if ((uintptr_t)flag % sizeof(int32_t) != 0)
+    return fail(PA_ERR_INVALID_ARG, "flag at %p is not 4-byte aligned", (void*)flag);
+  hipError_t e = pa::launch_copy_word((const int32_t*)workspace + pa::kCtrlAbort, flag,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode_check launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int pa_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {

@@ -61,6 +61,7 @@
 // rows (see prefix_items), then the sequences' own blocks as above.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdlib>
 #include <map>
 #include <mutex>
@@ -176,9 +177,10 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   __shared__ int nsplit;
   __shared__ int nsplit_long;
   __shared__ int npitems;
+  __shared__ int pitems_end;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.num_seqs;
-  const bool prefix = a.num_groups > 0;   // then S <= kLensCached (checked on the host)
+  bool prefix = a.num_groups > 0;   // then S <= kLensCached (checked on the host)
 
   for (int i = tid; i < kTailClasses; i += 1024) cls_off[i] = 0;
   if (tid == 0) {
@@ -187,6 +189,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     nsplit = 0;
     nsplit_long = 0;
     npitems = 0;
+    pitems_end = INT_MAX;
   }
   // Group g's bounds and prefix hint, read by thread g (for the first 1024
   // groups) together with the lengths, in one memory round trip.
@@ -195,6 +198,19 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     reg_lo = a.group_starts[tid];
     reg_hi = a.group_starts[tid + 1];
     reg_pb = a.prefix_blocks[tid];
+  }
+  // Groups must be ordered (group_starts non-decreasing), so that no two
+  // overlap: a sequence then belongs to one group at most and the prefix work
+  // list fits its S * num_parts_max entries.  Otherwise the groups are
+  // ignored and the batch is decoded plainly (the same result).
+  if (prefix) {
+    int bad = 0;
+    for (int g = tid; g < a.num_groups; g += 1024) {
+      const int lo = g < 1024 ? reg_lo : a.group_starts[g];
+      const int hi = g < 1024 ? reg_hi : a.group_starts[g + 1];
+      bad |= hi < lo;
+    }
+    prefix = block_sum_1024(bad, wave_sum) == 0;
   }
   // One pass over the context lengths (clamped), kept in LDS for the passes
   // below.  S * max_blocks fits in int32 (checked on the host).
@@ -215,8 +231,9 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     hi = min(g == tid ? reg_hi : a.group_starts[g + 1], S);
   };
   int pre_mine = 0;
+  const int num_groups = prefix ? a.num_groups : 0;
   if (prefix) {
-    for (int g = tid; g < a.num_groups; g += 1024) {
+    for (int g = tid; g < num_groups; g += 1024) {
       int lo, hi;
       group_range(g, lo, hi);
       if (hi - lo < 2) continue;
@@ -373,8 +390,12 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // Prefix work list: (first sequence, sequences, partition, prefix blocks)
   // for every run of per_item sequences of a group and every partition of
   // its prefix.  The order is arbitrary (it never changes the result).
+  // With ordered groups the list holds at most sum over groups of members *
+  // ceil(P / pbp) <= S * num_parts_max entries; the bound is checked anyway,
+  // so that no input can make the planner write past the list.
   if (prefix) {
-    for (int g = tid; g < a.num_groups; g += 1024) {
+    const int64_t cap = (int64_t)S * a.num_parts_max;
+    for (int g = tid; g < num_groups; g += 1024) {
       int lo, hi;
       group_range(g, lo, hi);
       if (hi - lo < 2) continue;
@@ -384,11 +405,17 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       for (int f = lo; f < hi; f += per_item) {
         const int n = min(per_item, hi - f);
         const int at = atomicAdd(&npitems, np);
+        if ((int64_t)at + np > cap) {
+          atomicMin(&pitems_end, at);
+          continue;
+        }
         for (int p = 0; p < np; ++p) a.ws_pitems[at + p] = make_int4(f, n, p, P);
       }
     }
     __syncthreads();
-    if (tid == 0) a.ws_ctrl[kCtrlPrefixItems] = npitems;
+    if (tid == 0) a.ws_ctrl[kCtrlPrefixItems] = min(npitems, pitems_end);
+  } else if (tid == 0) {
+    a.ws_ctrl[kCtrlPrefixItems] = 0;
   }
 }
 
@@ -871,8 +898,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // The workgroup's item for round r.  The list (longest items first) is
   // dealt, in snake order, for the first round only -- item b to workgroup
   // b -- and claimed after that: workgroup b takes the next unclaimed item of
-  // pool x = (b / 2) % kClaimPools (items NG + x, NG + x + kClaimPools, ...)
-  // until the pool is empty.  The two workgroups sharing a CU stream at different
+  // pool x = (b / 2) % npools (items NG + x, NG + x + npools, ...) until the
+  // pool is empty; npools = min(kClaimPools, NG / 2), so every pool has at
+  // least two workgroups claiming from it.  The two workgroups sharing a CU stream at different
   // speeds (the first dispatched one gets most of the memory pipeline), and
   // so do CUs on more or less loaded memory paths; claiming lets the faster
   // ones take more of the list, so the workgroups end closer together.
@@ -902,6 +930,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // workgroup NG-1-b when r is odd).
   auto item_of = [&](int r) -> int { return r * NG + ((r & 1) ? NG - 1 - bid : bid); };
   const bool claimed_rounds = total >= 2 * NG;
+  // Pools in use: kClaimPools, or fewer on a small grid, so that every pool
+  // has a claimer (pool x holds workgroups 2x and 2x + 1 among others).
+  const int npools = min(kClaimPools, max(1, NG >> kPoolShift));
   __shared__ int s_claim_busy[4];   // last round whose claim was started
   __shared__ int s_claim_tag[4];    // last round whose claim is published
   __shared__ int s_claim_item[4];
@@ -912,7 +943,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     if (lane == 0) {
       const int j = __hip_atomic_fetch_add(&claims[y * kClaimStride], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-      const int64_t cand = (int64_t)NG + y + (int64_t)j * kClaimPools;
+      const int64_t cand = (int64_t)NG + y + (int64_t)j * npools;
       it = cand < total ? (int)cand : total;
     }
     return __builtin_amdgcn_readfirstlane(it);
@@ -925,10 +956,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
       claimer = __hip_atomic_fetch_max(&s_claim_busy[slot], r, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP) < r;
     if (__builtin_amdgcn_readfirstlane(claimer)) {
-      const int x = (bid >> kPoolShift) & (kClaimPools - 1);
-      // Pool x holds workgroups 2x and 2x + 1 (mod 64); its lowest, 2x, is a
-      // first workgroup when 2x < num_cus.  Only then may the others stop
-      // early: a pool without a first workgroup (fewer than 64 CUs, or an
+      const int x = (bid >> kPoolShift) % npools;
+      // Pool x holds workgroups 2x and 2x + 1 (mod 2 * npools); its lowest,
+      // 2x, is a first workgroup when 2x < num_cus.  Only then may the others
+      // stop early: a pool without a first workgroup (fewer than 64 CUs, or an
       // unknown CU count) is emptied by whoever claims from it.
       if (a.num_cus > 0 && bid >= a.num_cus && (x << kPoolShift) < a.num_cus) {
         // A workgroup dispatched after its CU's first one streams slower
@@ -943,7 +974,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
         int stop = 0;
         if (lane == 0) {
           const int64_t left = (int64_t)total - NG - x;
-          const int64_t size = left > 0 ? (left + kClaimPools - 1) / kClaimPools : 0;
+          const int64_t size = left > 0 ? (left + npools - 1) / npools : 0;
           const int j = __hip_atomic_load(&claims[x * kClaimStride], __ATOMIC_RELAXED,
                                           __HIP_MEMORY_SCOPE_AGENT);
           stop = size - j < kLateStop;
@@ -1666,6 +1697,12 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (resident <= 0) return hipErrorInvalidDeviceFunction;
   const int64_t max_items = (int64_t)p.num_seqs * p.num_parts_max * p.num_kv_heads;
   p.decode_grid = (int)(max_items < resident ? max_items : resident);
+  // Test hook: PA_DECODE_GRID_OVERRIDE (read at every call) lowers the grid,
+  // so that tests reach the claim pools of a small grid on this device.
+  if (const char* o = getenv("PA_DECODE_GRID_OVERRIDE")) {
+    const int g = atoi(o);
+    if (g > 0 && g < p.decode_grid) p.decode_grid = g;
+  }
   p.num_cus = cu_count();
 
   p.prefix_rows = kPrefixRows;
@@ -1710,7 +1747,16 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void copy_word(const int32_t* src, int32_t* dst) {
+  if (threadIdx.x == 0) *dst = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+hipError_t launch_copy_word(const int32_t* src, int32_t* flag, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_word, dim3(1), dim3(64), 0, stream, src, flag);
+  return hipGetLastError();
+}
 
 bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t group) {
   (void)type;
@@ -1718,9 +1764,11 @@ bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t
          group >= 1 && group <= kMaxGroup;
 }
 
-hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
-                         int32_t block_size, bool vector_alu, hipStream_t stream,
-                         hipEvent_t ev_before, hipEvent_t ev_after, const WriteArgs* write) {
+hipError_t launch_decode(const DecodeParams& p, size_t params_bytes, KvType type,
+                         int32_t head_dim, int32_t block_size, bool vector_alu,
+                         hipStream_t stream, hipEvent_t ev_before, hipEvent_t ev_after,
+                         const WriteArgs* write) {
+  if (params_bytes != sizeof(DecodeParams)) return hipErrorInvalidImage;
   if (head_dim == 64 && block_size == 16)
     return launch_decode_shape<64, 16>(p, type, vector_alu, stream, ev_before, ev_after, write);
   if (head_dim == 64 && block_size == 32)

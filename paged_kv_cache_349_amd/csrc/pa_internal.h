@@ -63,7 +63,7 @@ constexpr int kCtrlLongSplits = 5;    // split sequences with more than kMergeSh
 constexpr int kMergeShort = 16;
 // Set by the decode kernel if one of its waits on other waves of its
 // workgroup did not end (a broken invariant; the output is then incomplete).
-// Tests read it; cleared by the planner.
+// Cleared by the planner; read through pa_decode_check.
 constexpr int kCtrlAbort = 20;
 // Claim counters of the matrix-core kernel's work list, one per pool
 // (workgroups b with b % kClaimPools == x claim from pool x), each in a
@@ -80,7 +80,22 @@ enum class KvType { F32 = 0, BF16 = 1 };
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int succeed();
 
-struct WriteArgs;   // pa_write_body.h
+// Arguments of one slot write (device pointers); the element loop is in
+// pa_write_body.h (device code).
+struct WriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  int64_t total;        // num_tokens * num_kv_heads * head_dim elements
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t v_tile;       // tokens per feature-major V sub-tile: 16 if 16 | block_size, else block_size
+  int64_t num_slots;    // num_blocks * block_size
+  int32_t elem_bytes;   // 2 (bf16) or 4 (fp32)
+};
 
 WriteArgs make_write_args(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                           const int32_t* slots, int32_t num_tokens, int32_t num_blocks,
@@ -100,15 +115,24 @@ hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const
                               hipStream_t stream);
 
 // Returns hipErrorInvalidValue for a (type, D, BS) combination without a kernel.
+// params_bytes is sizeof(DecodeParams) as the caller was compiled: if it is
+// not the size this launcher was compiled with (objects built from two
+// versions of this header and linked together), nothing is launched and
+// hipErrorInvalidImage is returned; the kernels would otherwise read the
+// pointers at the wrong offsets.
 // Non-null events are recorded on `stream` right before and right after the
 // attention kernel (not the planner or the merge), for kernel timing.
 // A non-null `write` is a slot write done in the planner's launch (its
 // workgroups other than the planner's), so the whole step takes one launch
 // less; the write and the plan are independent.
-hipError_t launch_decode(const DecodeParams& p, KvType type, int32_t head_dim,
-                         int32_t block_size, bool vector_alu, hipStream_t stream,
-                         hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
-                         const WriteArgs* write = nullptr);
+hipError_t launch_decode(const DecodeParams& p, size_t params_bytes, KvType type,
+                         int32_t head_dim, int32_t block_size, bool vector_alu,
+                         hipStream_t stream, hipEvent_t ev_before = nullptr,
+                         hipEvent_t ev_after = nullptr, const WriteArgs* write = nullptr);
+
+// Enqueue on `stream` a copy of the workspace's abort word (int32 at
+// ws_ctrl[kCtrlAbort]) into *flag (device or pinned host memory).
+hipError_t launch_copy_word(const int32_t* src, int32_t* flag, hipStream_t stream);
 
 bool decode_supported(KvType type, int32_t head_dim, int32_t block_size, int32_t group);
 

@@ -6,23 +6,9 @@
 
 #include <stdint.h>
 
-namespace pa {
+#include "pa_internal.h"
 
-// Arguments of one slot write (device pointers).
-struct WriteArgs {
-  void* k_cache;
-  void* v_cache;
-  const void* k_new;
-  const void* v_new;
-  const int32_t* slots;
-  int64_t total;        // num_tokens * num_kv_heads * head_dim elements
-  int32_t num_kv_heads;
-  int32_t head_dim;
-  int32_t block_size;
-  int32_t v_tile;       // tokens per feature-major V sub-tile: 16 if 16 | block_size, else block_size
-  int64_t num_slots;    // num_blocks * block_size
-  int32_t elem_bytes;   // 2 (bf16) or 4 (fp32)
-};
+namespace pa {
 
 // Elements first, first + stride, ... of the write: one per (token, kv head,
 // feature).  Reads of k_new/v_new and the K-cache writes are contiguous along

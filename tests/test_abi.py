@@ -200,3 +200,52 @@ def test_decode_step_argument_errors(lib):
     assert call(Hq=7) == 1          # Hq % Hkv
     assert call(ws=16) == 3         # workspace too small: nothing launched
     assert call(T=0, S=0) == 0      # empty step
+
+
+def test_decode_check_argument_errors(lib):
+    flag = 1 << 40
+    assert lib.pa_decode_check(None, 1 << 20, flag, None) == 1
+    assert lib.pa_decode_check(FAKE, 1 << 20, None, None) == 1
+    assert lib.pa_decode_check(FAKE + 16, 1 << 20, flag, None) == 3      # misaligned workspace
+    assert lib.pa_decode_check(FAKE, 64, flag, None) == 3                # smaller than any workspace
+    assert lib.pa_decode_check(FAKE, 1 << 20, flag + 2, None) == 1       # misaligned flag
+    assert lib.pa_last_error()
+
+
+# A host program that calls the decode launcher with a launch-parameter size
+# other than the one the library was compiled with, as an object built from
+# an older version of the internal header would: the launcher must refuse
+# before it launches anything (the check is the first thing it does, so this
+# runs without a GPU).
+_PARAMS_PROBE = r"""
+#include <cstdio>
+#include "pa_internal.h"
+int main() {
+  pa::DecodeParams p{};
+  const hipError_t bad = pa::launch_decode(p, sizeof(p) + 8, pa::KvType::BF16, 128, 16, false,
+                                           nullptr);
+  const hipError_t bad2 = pa::launch_decode(p, sizeof(p) - 8, pa::KvType::F32, 64, 32, true,
+                                            nullptr);
+  std::printf("%d %d %d\n", (int)bad, (int)bad2, (int)hipErrorInvalidImage);
+  return bad == hipErrorInvalidImage && bad2 == hipErrorInvalidImage ? 0 : 1;
+}
+"""
+
+
+def test_launcher_refuses_a_mismatched_parameter_layout(lib, tmp_path):
+    import shutil
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd import build as b
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "params_probe.cpp"
+    src.write_text(_PARAMS_PROBE)
+    exe = tmp_path / "params_probe"
+    libdir = os.path.dirname(pa.LIB_PATH)
+    subprocess.run([gxx, "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{b.ROCM}/include",
+                    f"-I{b.CSRC}", f"-I{b.INCLUDE}", str(src), "-o", str(exe), f"-L{libdir}", "-lpa",
+                    f"-Wl,-rpath,{libdir}", f"-L{b.ROCM}/lib", "-lamdhip64",
+                    f"-Wl,-rpath,{b.ROCM}/lib"], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr

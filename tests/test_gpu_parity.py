@@ -42,16 +42,11 @@ def _case(cfg, poison="nan", block_size=None, long_last=False, num_seqs=None):
     return w, k_ref, v_ref, ref
 
 
-# Word of the decode workspace where the kernel records a wait between its
-# waves that did not end (it then gives up rather than hang).
-_CTRL_ABORT_WORD = 20
-
-
-def _assert_no_abort():
-    import torch
+def _assert_no_abort(workspace=None):
+    """The decode kernel records a wait between its waves that did not end (it
+    then gives up rather than hang); pa_decode_check reads that word."""
     import paged_kv_cache_349_amd as pa
-    for ws in pa._workspaces.values():
-        assert int(ws[:128].view(torch.int32)[_CTRL_ABORT_WORD]) == 0, "decode kernel gave up a wait"
+    assert pa.decode_check(workspace) == 0, "decode kernel gave up a wait"
 
 
 def _run(w, **decode_kw):
@@ -335,6 +330,47 @@ def test_claim_pools_with_other_cu_counts(cus, monkeypatch):
         _say(f"  max-abs err {err:.3e}")
         assert np.isfinite(out).all()
         assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("grid", ["1", "3", "17", "40", "63", "100"])
+def test_small_decode_grids(grid, monkeypatch):
+    """The claim pools cover every item on grids smaller than two workgroups
+    per pool (fewer than 64 workgroups: a partitioned device), and any grid
+    gives the same bits as the default one (who computes an item never
+    changes its result)."""
+    for cfg in (2, 5):
+        w, _, _, ref = _case(cfg=cfg)
+        base = _run(w).out.cpu().numpy()
+        monkeypatch.setenv("PA_DECODE_GRID_OVERRIDE", grid)
+        _say(f"grid={grid} case {w.name}")
+        out = _run(w).out.cpu().numpy()
+        monkeypatch.delenv("PA_DECODE_GRID_OVERRIDE")
+        err = float(np.abs(out - ref).max())
+        _say(f"  max-abs err {err:.3e}")
+        assert err <= TOL["bf16"]
+        assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+
+
+def test_decode_check_on_a_caller_workspace():
+    """pa_decode_check reads the completion word of a workspace the caller
+    owns (not the binding's), on the call's stream."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    w, _, _, ref = _case(cfg=3)
+    d = upload(w)
+    pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    need = pa.workspace_bytes(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_blocks,
+                              w.block_size, pa.PA_DTYPE_BF16)
+    with torch.cuda.stream(side):
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+        pa.decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens,
+                  float(w.scale), w.block_size, stream=side, workspace=ws)
+    assert pa.decode_check(ws, stream=side) == 0
+    torch.cuda.synchronize()
+    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL["bf16"]
 
 
 RANDOM_CASES = list(range(24))

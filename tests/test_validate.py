@@ -57,3 +57,66 @@ def test_slots():
         pa.check_slots(np.array([0, 48 * 16], np.int32), 48, 16)
     with pytest.raises(ValueError, match="more than one token"):
         pa.check_slots(np.array([3, 7, 3], np.int32), 48, 16)
+
+
+def test_group_list_checks():
+    pa.check_groups([0, 8, 16, 16, 20], 20)
+    pa.check_groups([], 4)
+    with pytest.raises(ValueError, match="ordered"):
+        pa.check_groups([0, 20, 0, 20], 20)
+    with pytest.raises(ValueError, match="lie in"):
+        pa.check_groups([0, 8, 21], 20)
+    with pytest.raises(ValueError, match="lie in"):
+        pa.check_groups([-1, 8], 20)
+
+
+def test_binding_workspace_is_allocated_on_the_launch_stream(monkeypatch):
+    """A replaced workspace must not go back to the allocator for a stream
+    other than the one whose kernels may still use it: the binding allocates
+    it on the launch stream (checked here with a stand-in for torch)."""
+    import contextlib
+    events = []
+
+    class Stream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    class Tensor:
+        def __init__(self, n, on):
+            self.n, self.on = n, on
+
+        def numel(self):
+            return self.n
+
+    current = [None]
+
+    class Cuda:
+        @staticmethod
+        @contextlib.contextmanager
+        def stream(st):
+            prev, current[0] = current[0], st
+            events.append(("enter", st.cuda_stream))
+            yield
+            current[0] = prev
+
+    class FakeTorch:
+        cuda = Cuda
+        uint8 = "uint8"
+
+        @staticmethod
+        def empty(n, dtype=None, device=None):
+            return Tensor(n, current[0].cuda_stream if current[0] else None)
+
+    class Dev:
+        index = 0
+
+    monkeypatch.setattr(pa, "_torch", lambda: FakeTorch)
+    monkeypatch.setattr(pa, "_workspaces", {})
+    side = Stream(0xBEEF)
+    a = pa._workspace(Dev, side, 1000)
+    assert a.on == 0xBEEF
+    assert pa._workspace(Dev, side, 500) is a           # large enough: kept
+    b = pa._workspace(Dev, side, 5000)                   # replaced: again on the launch stream
+    assert b is not a and b.on == 0xBEEF
+    c = pa._workspace(Dev, Stream(7), 100)               # another stream has its own
+    assert c.on == 7 and pa._workspace(Dev, side, 10) is b
