@@ -335,20 +335,22 @@ def test_claim_pools_with_other_cu_counts(cus, monkeypatch):
 @pytest.mark.parametrize("grid", ["1", "3", "17", "40", "63", "100"])
 def test_small_decode_grids(grid, monkeypatch):
     """The claim pools cover every item on grids smaller than two workgroups
-    per pool (fewer than 64 workgroups: a partitioned device), and any grid
-    gives the same bits as the default one (who computes an item never
-    changes its result)."""
+    per pool (fewer than 64 workgroups: a partitioned device).  With the
+    library's partition choice (which depends on the grid) the output is
+    within the bar; with a fixed partition size it is the same bits as on the
+    default grid (who computes an item never changes its result)."""
     for cfg in (2, 5):
         w, _, _, ref = _case(cfg=cfg)
-        base = _run(w).out.cpu().numpy()
+        base = _run(w, partition_tokens=256).out.cpu().numpy()
         monkeypatch.setenv("PA_DECODE_GRID_OVERRIDE", grid)
         _say(f"grid={grid} case {w.name}")
         out = _run(w).out.cpu().numpy()
+        fixed = _run(w, partition_tokens=256).out.cpu().numpy()
         monkeypatch.delenv("PA_DECODE_GRID_OVERRIDE")
         err = float(np.abs(out - ref).max())
         _say(f"  max-abs err {err:.3e}")
         assert err <= TOL["bf16"]
-        assert np.array_equal(out.view(np.uint32), base.view(np.uint32))
+        assert np.array_equal(fixed.view(np.uint32), base.view(np.uint32))
 
 
 def test_decode_check_on_a_caller_workspace():
