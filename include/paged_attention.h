@@ -273,7 +273,9 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_hea
  * of every call).  This call enqueues on `stream` a copy of that word into
  * *flag: 0 = every wait ended, 1 = the output of that call is incomplete.
  *   workspace   the workspace the decode call used (device, 256-byte aligned,
- *               workspace_bytes >= 4224, as any decode workspace is)
+ *               workspace_bytes >= 4224, as any decode workspace is); NULL
+ *               with workspace_bytes == 0 means pa_decode_noalloc's array
+ *               on the current device
  *   flag        one int32, device memory or pinned host memory (4-byte
  *               aligned); valid once `stream` has reached this point
  * Errors (reported before anything is enqueued): a null pointer or a
@@ -281,6 +283,32 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_hea
  * is PA_ERR_WORKSPACE.  The call allocates nothing and does not synchronise.
  */
 int pa_decode_check(const void* workspace, size_t workspace_bytes, int32_t* flag, void* stream);
+
+/*
+ * pa_decode for callers that cannot allocate or pass device memory for a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments as pa_decode without the
+ * workspace, and the same result up to rounding: bit for bit whenever
+ * pa_decode's own workspace for these shapes would fit in the array;
+ * otherwise the context split may use longer partitions.  The workspace is
+ * the library's own fixed device array of 64 MiB, one per device: the HIP
+ * runtime reserves it when it loads the library's device code on that
+ * device, and it is held until the process ends; the call itself allocates
+ * nothing.
+ * Shapes whose workspace does not fit in 64 MiB even with 8192-token
+ * partitions (roughly num_seqs * num_heads * ceil(max_blocks_per_seq *
+ * block_size / 8192) * (head_dim + 2) * 4 bytes) are rejected with
+ * PA_ERR_WORKSPACE before anything is enqueued; other argument errors are
+ * pa_decode's.  Every call on a device uses that device's one array: calls
+ * that may overlap on one device (different streams, or threads) race and
+ * must not be made.  pa_decode_check(NULL, 0, flag, stream) reports the
+ * completion of the last such call on the current device.
+ */
+int pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, int32_t kv_dtype, void* stream);
 
 /* Tokens per partition that pa_decode picks for these shapes (0 if invalid). */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,

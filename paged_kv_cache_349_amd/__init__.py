@@ -54,6 +54,8 @@ _SIGNATURES = {
                                 [_vp, ctypes.c_size_t, _c_int, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (ctypes.c_size_t, [_c_int] * 8),
     "pa_decode_check": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float] +
+                          [_c_int] * 8 + [_vp]),
     "pa_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "pa_probe_read_tiles": (ctypes.c_int, [_vp, _vp, _vp, _c_int, _c_int, ctypes.c_int64, _vp,
                                            _vp]),
@@ -302,19 +304,25 @@ def _workspace(dev, stream, nbytes):
     return ws
 
 
-def decode_check(workspace=None, stream=None, device=None) -> int:
+def decode_check(workspace=None, stream=None, device=None, *, noalloc=False) -> int:
     """Abort word of the last decode call that used `workspace` (by default the
-    binding's own workspace for `device` and `stream`): 0 if that call's kernels
-    completed every wait, 1 if one gave up a wait (its output is then
-    incomplete).  Enqueues the read on the stream and synchronises it."""
+    binding's own workspace for `device` and `stream`; with noalloc=True the
+    array of decode_noalloc): 0 if that call's kernels completed every wait, 1
+    if one gave up a wait (its output is then incomplete).  Enqueues the read
+    on the stream and synchronises it."""
     torch = _torch()
     lib = load_library()
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     st = _stream_of(dev, stream)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    if noalloc:
+        with torch.cuda.device(dev):
+            _check(lib.pa_decode_check(None, 0, flag.data_ptr(), st.cuda_stream))
+        st.synchronize()
+        return int(flag.item())
     if workspace is None:
         workspace = _workspaces.get((dev.index, st.cuda_stream))
         _need(workspace is not None, "no decode has run on this device and stream")
-    flag = torch.full((1,), -1, dtype=torch.int32, device=dev)
     _check(lib.pa_decode_check(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                flag.data_ptr(), st.cuda_stream))
     st.synchronize()
@@ -356,6 +364,33 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
                             block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, S,
                             Hq, Hkv, D, max_blocks, NB, code, ws_ptr, ws_len, partition_tokens,
                             flags, sh))
+    return out
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                   stream=None):
+    """decode() through pa_decode_noalloc: the library's fixed per-device array is
+    the workspace, so neither the binding nor the library allocates anything.
+    Calls that may overlap on one device must not be made."""
+    torch = _torch()
+    lib = load_library()
+    dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, bs, D = _pool_shape(k_cache, v_cache)
+    _need(bs == block_size, f"block_size={block_size} but k_cache has {bs}")
+    _need(q.dim() == 3 and q.shape[2] == D, "q must be [S, Hq, D]")
+    S, Hq, _ = q.shape
+    _need(q.dtype == k_cache.dtype, "q and caches must share a dtype")
+    _need(out.dtype == torch.float32 and tuple(out.shape) == (S, Hq, D), "out: float32 [S, Hq, D]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.shape[0] == S, "block_tables: int32 [S, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens: int32 [S]")
+    with torch.cuda.device(dev):
+        _check(lib.pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), block_tables.data_ptr(),
+                                     context_lens.data_ptr(), float(scale), bs, S, Hq, Hkv, D,
+                                     block_tables.shape[1], NB, _dtype_code(k_cache),
+                                     _stream_handle(dev, stream)))
     return out
 
 
@@ -476,6 +511,6 @@ def kernel_timing_end():
 
 
 __all__ = ["v_pool_shape", "write_kv", "decode", "decode_step", "decode_shared_prefix",
-           "decode_check", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
+           "decode_check", "decode_noalloc", "copy_blocks", "swap_blocks", "workspace_bytes", "load_library",
            "LIB_PATH", "PagedAttentionError", "kernel_timing_begin", "kernel_timing_end",
            "check_slots", "check_tables", "check_groups"]

@@ -22,7 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libpa.so")
 
 ARCH = "gfx950"
-SOURCES = ["pa_api.cpp", "block_manager.cpp", "pa_write_kv.hip", "pa_blocks.hip", "pa_probe.hip", "pa_decode.hip"]
+SOURCES = ["pa_api.cpp", "block_manager.cpp", "pa_write_kv.hip", "pa_blocks.hip", "pa_probe.hip",
+           "pa_decode.hip", "pa_noalloc.hip"]
 # Packed fp32 instructions are kept out of the device code.
 # MFMA accumulators are kept in ordinary VGPRs, where the softmax rescale can
 # reach them without copies to and from the accumulation registers.

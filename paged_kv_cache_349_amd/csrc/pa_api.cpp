@@ -146,7 +146,7 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
                          size_t workspace_bytes, int32_t partition_tokens, int32_t flags,
                          const int32_t* group_starts, const int32_t* prefix_blocks,
                          int32_t num_groups, bool prefix, void* stream,
-                         const pa::WriteArgs* write = nullptr) {
+                         const pa::WriteArgs* write = nullptr, int32_t floor_tokens = 0) {
   if (kv_dtype != PA_DTYPE_F32 && kv_dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "kv_dtype=%d is neither F32 nor BF16", kv_dtype);
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
@@ -171,7 +171,10 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
       (int64_t)num_seqs * num_heads * head_dim > INT32_MAX * 4LL)
     return fail(PA_ERR_UNSUPPORTED, "shape too large");
   const bool adaptive = partition_tokens == 0;
-  if (adaptive) partition_tokens = min_partition_tokens(block_size);
+  if (adaptive) {
+    partition_tokens = min_partition_tokens(block_size);
+    if (floor_tokens > partition_tokens) partition_tokens = floor_tokens;
+  }
   if (partition_tokens < block_size || partition_tokens % block_size != 0)
     return fail(PA_ERR_INVALID_ARG, "partition_tokens=%d is not a positive multiple of %d",
                 partition_tokens, block_size);
@@ -246,6 +249,27 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
 }
 
 }  // namespace
+
+namespace pa {
+
+int decode_with_floor(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, int32_t kv_dtype, void* workspace,
+                      size_t workspace_bytes, int32_t floor_tokens, void* stream) {
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                       num_blocks, kv_dtype, workspace, workspace_bytes, 0, 0, nullptr, nullptr,
+                       0, false, stream, nullptr, floor_tokens);
+}
+
+int32_t adaptive_partition_limits(int32_t block_size, int32_t* max_tokens) {
+  *max_tokens = kMaxPartitionTokens < block_size ? block_size : kMaxPartitionTokens;
+  return min_partition_tokens(block_size);
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -447,7 +471,16 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
 }
 
 int pa_decode_check(const void* workspace, size_t workspace_bytes, int32_t* flag, void* stream) {
-  if (!workspace || !flag) return fail(PA_ERR_INVALID_ARG, "null workspace or flag pointer");
+  if (!flag) return fail(PA_ERR_INVALID_ARG, "null flag pointer");
+  if (!workspace && workspace_bytes == 0) {
+    // The scratch of pa_decode_noalloc on the current device.
+    void* ptr = nullptr;
+    const int st = pa::noalloc_scratch(&ptr, &workspace_bytes);
+    if (st != PA_OK) return st;
+    workspace = ptr;
+  }
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "null workspace with workspace_bytes=%zu",
+                              workspace_bytes);
   if ((uintptr_t)workspace % 256 != 0)
     return fail(PA_ERR_WORKSPACE, "workspace at %p must be 256-byte aligned", workspace);
   if (workspace_bytes < (size_t)pa::kCtrlSize * sizeof(int32_t))

@@ -130,6 +130,24 @@ hipError_t launch_decode(const DecodeParams& p, size_t params_bytes, KvType type
                          hipStream_t stream, hipEvent_t ev_before = nullptr,
                          hipEvent_t ev_after = nullptr, const WriteArgs* write = nullptr);
 
+// pa_decode with the library's adaptive partition size, its smallest choice
+// raised to floor_tokens (a power-of-two multiple of the default smallest):
+// the workspace then needs fewer partition states.  Same checks and status
+// codes as pa_decode.
+int decode_with_floor(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t num_blocks, int32_t kv_dtype, void* workspace,
+                      size_t workspace_bytes, int32_t floor_tokens, void* stream);
+
+// Smallest and (in *max_tokens) largest partition the adaptive choice may take.
+int32_t adaptive_partition_limits(int32_t block_size, int32_t* max_tokens);
+
+// Device address and size of pa_decode_noalloc's scratch on the current
+// device (pa_noalloc.hip); a pa_status.
+int noalloc_scratch(void** ptr, size_t* bytes);
+
 // Enqueue on `stream` a copy of the workspace's abort word (int32 at
 // ws_ctrl[kCtrlAbort]) into *flag (device or pinned host memory).
 hipError_t launch_copy_word(const int32_t* src, int32_t* flag, hipStream_t stream);

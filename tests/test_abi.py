@@ -249,3 +249,17 @@ def test_launcher_refuses_a_mismatched_parameter_layout(lib, tmp_path):
                     f"-Wl,-rpath,{b.ROCM}/lib"], check=True, capture_output=True, text=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_decode_noalloc_argument_errors(lib):
+    """Checks that return before the library's array is touched (no GPU needed)."""
+    def call(S=4, Hq=8, Hkv=2, D=128, maxb=8, bs=16, dt=1, out=FAKE):
+        return lib.pa_decode_noalloc(out, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, bs, S, Hq, Hkv, D,
+                                     maxb, 64, dt, None)
+    assert call(S=4096, Hq=64, Hkv=8, maxb=2048) == 3     # too large for the array
+    assert lib.pa_last_error().startswith(b"these shapes need")
+    assert call(Hq=6, Hkv=4) == 1
+    assert call(D=96) == 2
+    assert call(dt=5) == 2
+    assert call(out=None) == 1
+    assert call(S=0, out=None) == 0                       # empty batch: nothing to do
