@@ -231,6 +231,158 @@ def bench_block_size_32(args, dev, stream):
     }
 
 
+def bench_configs(args, dev, stream, which):
+    """The other workloads (gqa, skewed long context, parallel sampling), cold.
+
+    Their K/V (166-285 MB) is about the size of the 256 MB last-level cache,
+    so every timed launch follows a read of 1 GiB that evicts it (outside the
+    event pair; a read leaves no dirty lines for the decode to write back).
+    Per workload:
+      step_us_warm     pa_decode_step (the parallel-sampling workload: write +
+                       pa_decode_shared_prefix) back to back, warm
+      call_us_cold     one decode call (planner, attention kernel, merge)
+      kernel_us_cold   the attention kernel alone (the library's events)
+      *_frac           algorithmic bytes (distinct live K/V + q + out + table)
+                       / time / 8 TB/s
+      contig_*         the same calls over the tokens packed sequence by
+                       sequence (identity-like tables), cold, alternating
+      max_abs_err      output of the timed call against the float64 oracle
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd import workloads as wl
+    from paged_kv_cache_349_amd.device_io import upload
+
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    n_cold = max(5, args.config_iters)
+    res = {}
+    for cfg in which:
+        w = wl.make_config(cfg)
+        d = upload(w, dev)
+        pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+        prefix = cfg == 4
+        if prefix:
+            gs, pbl = w.prefix_groups()
+            gsd, pbd = torch.from_numpy(gs).to(dev), torch.from_numpy(pbl).to(dev)
+
+        def call(dd=d, ww=w, shared=prefix):
+            if shared:
+                pa.decode_shared_prefix(dd.out, dd.q, dd.k_cache, dd.v_cache, dd.block_tables,
+                                        dd.context_lens, gsd, pbd, float(ww.scale), ww.block_size)
+            else:
+                pa.decode(dd.out, dd.q, dd.k_cache, dd.v_cache, dd.block_tables,
+                          dd.context_lens, float(ww.scale), ww.block_size)
+
+        def step():
+            if prefix:
+                pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+                call()
+            else:
+                pa.decode_step(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping, d.out,
+                               d.q, d.block_tables, d.context_lens, float(w.scale), w.block_size)
+
+        def cold_calls(fn, n):
+            ts = []
+            for _ in range(n):
+                flush.sum()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            return ts
+
+        def cold_kernel(fn, n):
+            pa.kernel_timing_begin(n)
+            for _ in range(n):
+                flush.sum()
+                fn()
+            torch.cuda.synchronize()
+            ms, k = pa.kernel_timing_end()
+            return ms * 1e3 / k
+
+        def warm_kernel(fn, n):
+            pa.kernel_timing_begin(n)
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            ms, k = pa.kernel_timing_end()
+            return ms * 1e3 / k
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        K = max(20, min(args.steps, 200))
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t0) * 1e6 / K
+        kern_warm = warm_kernel(call, K)
+        calls = cold_calls(call, n_cold)
+        kern_cold = cold_kernel(call, n_cold)
+        out = d.out.cpu().numpy()
+        k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping,
+                                       w.block_size)
+        ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale,
+                            w.block_size, w.kv_dtype)
+        err = float(np.abs(out - ref).max())
+        alg = w.kv_bytes_unique() + w.small_bytes()
+        frac = lambda us: round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        call_cold = statistics.median(calls)
+        rec = {
+            "num_seqs": w.num_seqs, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size,
+            "context_tokens": int(w.context_lens.sum()), "max_context": int(w.context_lens.max()),
+            "call": "pa_decode_shared_prefix" if prefix else "pa_decode",
+            "algorithmic_bytes": alg, "kv_bytes_logical": w.kv_bytes_logical(),
+            "step_us_warm": round(step_us, 2),
+            "call_us_cold": round(call_cold, 2),
+            "call_us_cold_p90": round(float(np.percentile(calls, 90)), 2),
+            "kernel_us_cold": round(kern_cold, 2), "kernel_us_warm": round(kern_warm, 2),
+            "kernel_frac_cold": frac(kern_cold), "call_frac_cold": frac(call_cold),
+            "kernel_frac_warm": frac(kern_warm), "step_frac_warm": frac(step_us),
+            "seq_steps_per_s": round(w.num_seqs / (step_us * 1e-6), 1),
+            "max_abs_err": float(f"{err:.3e}"),
+        }
+        if prefix:
+            plain = lambda: call(shared=False)
+            rec["plain_decode_call_us_cold"] = round(statistics.median(cold_calls(plain, n_cold)), 2)
+            rec["plain_decode_kernel_us_cold"] = round(cold_kernel(plain, n_cold), 2)
+        if not args.no_contig:
+            wc = wl.to_contiguous(w)
+            dc = upload(wc, dev)
+            pa.write_kv(dc.k_cache, dc.v_cache, dc.k_new, dc.v_new, dc.slot_mapping)
+            pc, cc = [], []
+            for _ in range(n_cold):
+                pc += cold_calls(lambda: call(shared=False), 1)
+                cc += cold_calls(lambda: call(dc, wc, False), 1)
+            rec["contig_call_us_cold"] = round(statistics.median(cc), 2)
+            rec["paged_call_us_cold"] = round(statistics.median(pc), 2)
+            rec["paged_overhead_vs_contig"] = round(statistics.median(pc) / statistics.median(cc) - 1, 4)
+            kp = cold_kernel(lambda: call(shared=False), n_cold)
+            kc = cold_kernel(lambda: call(dc, wc, False), n_cold)
+            rec["paged_overhead_vs_contig_kernel"] = round(kp / kc - 1, 4)
+            if prefix:
+                rec["contig_note"] = ("packed run gives every sample its own copy of the prompt "
+                                      "(plain pa_decode on both sides): context only")
+            del dc
+        log(f"{w.name}: step {step_us:.1f} us warm; call {call_cold:.1f} us cold "
+            f"({rec['call_frac_cold']:.3f}); kernel {kern_cold:.1f} us cold "
+            f"({rec['kernel_frac_cold']:.3f}), {kern_warm:.1f} us warm; err {err:.2e}"
+            + (f"; paged vs packed {rec['paged_overhead_vs_contig']:+.2%} per call, "
+               f"{rec['paged_overhead_vs_contig_kernel']:+.2%} per kernel"
+               if "paged_overhead_vs_contig" in rec else ""))
+        res[w.name] = rec
+        del d
+    del flush
+    return res
+
+
 PCIE_GEN5_X16_GBPS = 63.0   # 32 GT/s x 16 lanes, 128b/130b coding, per direction
 
 
@@ -335,6 +487,13 @@ def parse_args():
                    help="skip the block-size-32 variant of the large-batch workload")
     p.add_argument("--no-shared-prefix", action="store_true",
                    help="skip the shared-prefix decode measurement (parallel-sampling workload)")
+    p.add_argument("--configs", default="2,3,4",
+                   help="comma-separated other workloads measured cold in the `configs` record "
+                        "('' = none)")
+    p.add_argument("--config-iters", type=int, default=20,
+                   help="cold launches per measurement in the `configs` record")
+    p.add_argument("--configs-only", action="store_true",
+                   help="run only the `configs` record (for profiling its cold launches)")
     p.add_argument("--shared-prefix", action="store_true",
                    help="time pa_decode_shared_prefix instead of pa_decode in the main loop "
                         "(groups of consecutive sequences with common leading blocks)")
@@ -365,6 +524,11 @@ def main() -> int:
     pa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    which = [int(c) for c in args.configs.split(",") if c.strip()]
+    if args.configs_only:
+        res = bench_configs(args, dev, torch.cuda.current_stream(dev), which)
+        print(json.dumps({"configs": res}), flush=True)
+        return 0
 
     t = time.perf_counter()
     w = wl.make_config(args.config, block_size=args.block_size, seed=args.seed)
@@ -574,6 +738,9 @@ def main() -> int:
 
     if not args.no_shared_prefix and args.config == 5:
         result["shared_prefix"] = bench_shared_prefix(args, dev, stream)
+
+    if which and args.config == 5 and not args.shared_prefix:
+        result["configs"] = bench_configs(args, dev, stream, which)
 
     if not args.no_blocks:
         result["blocks"] = bench_blocks(args, w, d, dev, stream)

@@ -50,8 +50,9 @@
 // 16 tokens of a block), so each lane loads 4 consecutive tokens of one
 // feature (8 bytes) for the PV A operand and every 16-token position reads
 // one contiguous 4 KB span of K and one of V (D = 128, bf16).
-// P is rounded to bf16 for the PV product; the softmax denominator sums those
-// same rounded weights, so the output is an exact convex combination of them.
+// P enters the PV product as two bf16 operands, hi = bf16(P) and lo =
+// bf16(P - hi) (see split_weight), so the weights keep about 16 bits; the
+// softmax denominator sums the same hi + lo.
 //
 // Vector-ALU kernel (fp32, and bf16 on request): the same items and merge;
 // scores by lanes over tokens, weighted values by lanes over features.
@@ -91,10 +92,30 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite, >= 0).
+// fp32 -> bf16 bits, round to nearest even (finite inputs; the sign bit rides
+// along, so negative values round by magnitude too).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Softmax weights enter the PV matrix product as bf16 operands.  A weight p
+// in [0, 1] is split into hi = bf16(p) and lo = bf16(p - hi): p - hi is exact
+// in fp32 (hi is within 2^-8 of p, relatively), so hi + lo carries p to about
+// 2^-16 relative instead of the 2^-9 of hi alone, at the price of a second
+// PV product per sub-block (the kernel is bound by HBM, not by the matrix
+// cores).  The softmax denominator sums hi + lo, the weights the two products
+// apply together (`sum`).
+struct SplitWeight {
+  short hi, lo;
+  float sum;
+};
+
+__device__ __forceinline__ SplitWeight split_weight(float p) {
+  const uint32_t h = f32_to_bf16_bits(p);
+  const float ph = bf16_bits_to_f32(h);
+  const uint32_t l = f32_to_bf16_bits(p - ph);
+  return SplitWeight{(short)h, (short)l, ph + bf16_bits_to_f32(l)};
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
@@ -162,9 +183,107 @@ __device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
 }
 
 constexpr int kPartChoices = 8;
-
 constexpr int kLensCached = 8192;   // context lengths the planner keeps in LDS
 constexpr int kDirectItems = 4;     // full partitions a planner thread lists itself
+
+// Partition size: the largest pb = part_blocks_min * 2^k (<= part_blocks_max)
+// whose partitions are each at most 1/balance of one workgroup's share of
+// `work` blocks over `grid` workgroups (balance 0: always the smallest).
+__device__ __forceinline__ int choose_part_blocks(const DecodeParams& a, int64_t work,
+                                                  int64_t grid, int balance) {
+  int pb = a.part_blocks_min;
+  if (balance > 0) {
+    const int64_t share = work * a.num_kv_heads / ((grid > 0 ? grid : 1) * balance);
+    for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share && pb * 2 <= a.part_blocks_max;
+         ++k)
+      pb *= 2;
+  }
+  return pb;
+}
+
+// Sum over a wave (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// The planner of a batch of at most 64 sequences without shared prefixes, in
+// one wave with no barrier: lane s plans sequence s.  Its lists are those of
+// plan_body (same partition size, same items, same split sequences) except
+// for the order of the partial last partitions -- here by decreasing size,
+// ties by sequence -- and of the split list, neither of which changes a
+// result.
+template <int BS>
+__device__ __forceinline__ void plan_small(const DecodeParams& a) {
+  const int lane = threadIdx.x & 63;
+  const int S = a.num_seqs;
+  const bool live = lane < S;
+  const int L = live ? clamp_len(a, lane, BS) : 0;
+  const int nblk = (L + BS - 1) / BS;
+  const int pb = choose_part_blocks(a, wave_sum(nblk), a.decode_grid, a.balance);
+  const int pbp = choose_part_blocks(a, 0, a.decode_grid / 2, 0);
+  // Full partitions in sequence order (an empty sequence gets one item that
+  // zeroes its output); a sequence's first kDirectItems are listed by its
+  // lane, any further ones by all lanes together.
+  const int nfull = live ? (nblk == 0 ? 1 : nblk / pb) : 0;
+  int incl = nfull;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  const int base = incl - nfull;
+  const int n_full = __shfl(incl, 63, 64);
+  for (int p = 0; p < min(nfull, kDirectItems); ++p)
+    a.ws_items[base + p] = make_int4(lane, p, L, 0);
+  if (__builtin_amdgcn_ballot_w64(nfull > kDirectItems)) {
+    for (int j = 0; j < S; ++j) {
+      const int nj = __builtin_amdgcn_readlane(nfull, j);
+      if (nj <= kDirectItems) continue;
+      const int bj = __builtin_amdgcn_readlane(base, j);
+      const int Lj = __builtin_amdgcn_readlane(L, j);
+      for (int p = kDirectItems + lane; p < nj; p += 64) a.ws_items[bj + p] = make_int4(j, p, Lj, 0);
+    }
+  }
+  // Partial last partitions after all full ones, by decreasing size.
+  const int rem = nblk % pb;
+  const bool tail = live && rem != 0;
+  int rank = 0;
+  for (int j = 0; j < S; ++j) {
+    const int rj = __builtin_amdgcn_readlane(rem, j);
+    rank += rj != 0 && (rj > rem || (rj == rem && j < lane));
+  }
+  if (tail) a.ws_items[n_full + rank] = make_int4(lane, nblk / pb, L, 0);
+  // Sequences whose partition states are merged: up to kMergeShort
+  // partitions from the front of the split list, longer ones from the back.
+  const int nparts = (nblk + pb - 1) / pb;
+  const uint64_t below = (1ull << lane) - 1;
+  const uint64_t short_split = __builtin_amdgcn_ballot_w64(live && nparts > 1 && nparts <= kMergeShort);
+  const uint64_t long_split = __builtin_amdgcn_ballot_w64(live && nparts > kMergeShort);
+  if (live && nparts > 1) {
+    const int at = nparts <= kMergeShort ? __builtin_popcountll(short_split & below)
+                                         : S - 1 - __builtin_popcountll(long_split & below);
+    a.ws_split[at] = make_int2(lane, nparts);
+  }
+  const int n_tail = __builtin_popcountll(__builtin_amdgcn_ballot_w64(tail));
+  if (lane == 0) {
+    a.ws_ctrl[kCtrlEntries] = n_full + n_tail;
+    a.ws_ctrl[kCtrlPartBlocks] = pb;
+    a.ws_ctrl[kCtrlSplits] = __builtin_popcountll(short_split);
+    a.ws_ctrl[kCtrlPrefixItems] = 0;
+    a.ws_ctrl[kCtrlPrefixPart] = pbp;
+    a.ws_ctrl[kCtrlLongSplits] = __builtin_popcountll(long_split);
+    a.ws_ctrl[kCtrlAbort] = 0;
+  }
+  if (lane < kClaimPools) a.ws_ctrl[kCtrlClaims + lane * kClaimStride] = 0;
+}
+
+// Whether plan_small plans this batch.
+__host__ __device__ __forceinline__ bool small_plan(const DecodeParams& a) {
+  return a.num_seqs <= 64 && a.num_groups == 0;
+}
+
 
 __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size) {
   __shared__ int lens_c[kLensCached];
@@ -252,27 +371,16 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     mine += (len_of(s) + block_size - 1) / block_size - start_of(s);
   const int64_t total = block_sum_1024(mine, wave_sum);
 
-  // Partition size: the largest pb = part_blocks_min * 2^k (<= part_blocks_max)
-  // whose partitions are each at most 1/balance of one workgroup's share of
-  // all blocks.  Long partitions mean few partition states to merge; short
-  // ones spread a long context over many workgroups.  Prefix partitions are
+  // Partition size (choose_part_blocks).  Long partitions mean few partition
+  // states to merge; short ones spread a long context over many workgroups.
+  // Prefix partitions are
   // sized from the prefix work alone, for about one prefix item per CU (half
   // the resident workgroups): the CU's other workgroup streams own blocks
   // meanwhile.  Measured on the parallel-sampling workload (16 prompts of 128
   // blocks, 8 KV heads, 512 workgroups): 64-block prefix partitions 68 us per
   // call, 32 blocks 74 us, 128 blocks 78 us.
-  auto pick = [&](int64_t work, int64_t grid, int balance) {
-    int pb = a.part_blocks_min;
-    if (balance > 0) {
-      const int64_t share = work * a.num_kv_heads / ((grid > 0 ? grid : 1) * balance);
-      for (int k = 0; k < kPartChoices && (int64_t)pb * 2 <= share &&
-                      pb * 2 <= a.part_blocks_max; ++k)
-        pb *= 2;
-    }
-    return pb;
-  };
-  const int pb = pick(total, a.decode_grid, a.balance);
-  const int pbp = pick(pre_total, a.decode_grid / 2, a.balance > 0 ? 1 : 0);
+  const int pb = choose_part_blocks(a, total, a.decode_grid, a.balance);
+  const int pbp = choose_part_blocks(a, pre_total, a.decode_grid / 2, a.balance > 0 ? 1 : 0);
   if (tid == 0) {
     a.ws_ctrl[kCtrlPartBlocks] = pb;
     a.ws_ctrl[kCtrlPrefixPart] = pbp;
@@ -425,12 +533,20 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 // it are shifts.
 template <int BS>
 __global__ __launch_bounds__(1024) void plan_items(DecodeParams a) {
+  if (small_plan(a)) {
+    if (threadIdx.x < 64) plan_small<BS>(a);   // launched with one wave for such batches
+    return;
+  }
   plan_body(a, BS);
 }
 
 template <typename E, int BS>
 __global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, WriteArgs w) {
   if (blockIdx.x == 0) {
+    if (small_plan(a)) {
+      if (threadIdx.x < 64) plan_small<BS>(a);
+      return;
+    }
     plan_body(a, BS);
     return;
   }
@@ -757,15 +873,16 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
         const float mref = mnew == kNegInf ? 0.f : mnew;
         const float alpha = exp2_fast(m[hh] - mref);
         m[hh] = mnew;
-        i16x4 pw[Tile<D, 16>::SB];
+        i16x4 pw[Tile<D, 16>::SB], pl[Tile<D, 16>::SB];
         float psum = 0.f;
 #pragma unroll
         for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
-            pw[sb][rr] = (short)bits;
-            psum += bf16_bits_to_f32(bits);
+            const SplitWeight sw = split_weight(exp2_fast(sc[sb][rr] - mref));
+            pw[sb][rr] = sw.hi;
+            pl[sb][rr] = sw.lo;
+            psum += sw.sum;
           }
         lsum[hh] = lsum[hh] * alpha + psum;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
@@ -775,9 +892,12 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
 #pragma unroll
         for (int i = 0; i < D / 16; ++i)
 #pragma unroll
-          for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
+          for (int sb = 0; sb < Tile<D, 16>::SB; ++sb) {
             acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[hh][i],
                                                                    0, 0, 0);
+            acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pl[sb], acc[hh][i],
+                                                                   0, 0, 0);
+          }
       }
     };
 
@@ -1127,15 +1247,16 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     const float mref = mnew == kNegInf ? 0.f : mnew;
     const float alpha = exp2_fast(m - mref);       // 0 on the first live block
     m = mnew;
-    i16x4 pw[Tile<D, 16>::SB];
+    i16x4 pw[Tile<D, 16>::SB], pl[Tile<D, 16>::SB];
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t bits = f32_to_bf16_bits(exp2_fast(sc[sb][rr] - mref));
-        pw[sb][rr] = (short)bits;
-        psum += bf16_bits_to_f32(bits);
+        const SplitWeight sw = split_weight(exp2_fast(sc[sb][rr] - mref));
+        pw[sb][rr] = sw.hi;
+        pl[sb][rr] = sw.lo;
+        psum += sw.sum;
       }
     lsum = lsum * alpha + psum;
     // Rescale every time (alpha is exactly 1 while a head's running max holds,
@@ -1159,8 +1280,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i)
 #pragma unroll
-      for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
+      for (int sb = 0; sb < Tile<D, 16>::SB; ++sb) {
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pl[sb], acc[i], 0, 0, 0);
+      }
   };
 
   // End of an item, without a barrier: the wave stores its state in the
@@ -1715,7 +1838,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
     else
       hipLaunchKernelGGL((write_and_plan<uint32_t, BS>), grid, dim3(1024), 0, stream, p, *write);
   } else {
-    hipLaunchKernelGGL(plan_items<BS>, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(plan_items<BS>, dim3(1), dim3(small_plan(p) ? 64 : 1024), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

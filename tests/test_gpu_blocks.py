@@ -16,6 +16,18 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
+# The stated bars above, and a regression line far below them: the bf16
+# kernels carry the softmax weights to about 16 bits (a hi/lo pair of bf16
+# operands), so their error against the float64 oracle is ~1e-6; a change that
+# loses that precision fails here long before it reaches the bar.
+REGRESSION = {"f32": 1e-5, "bf16": 1e-4}
+
+
+def _bars(err, dt, *msg):
+    """Assert the stated bar and the regression line for KV dtype `dt`."""
+    assert err <= TOL[dt], (err, TOL[dt], *msg)
+    assert err <= REGRESSION[dt], ("above the regression line", err, REGRESSION[dt], *msg)
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -214,7 +226,7 @@ def test_serving_loop_with_sharing_cow_and_swap(dt):
         assert np.array_equal(_raw(_np(vd, dt)), _raw(v)), step
         err = float(np.abs(out.cpu().numpy() - ref).max())
         _say(f"  step {step}: {len(active)} seqs, {len(cs)} copies, max-abs err {err:.2e}")
-        assert err <= TOL[dt], (step, err)
+        _bars(err, dt, (step, err))
         if dt == "bf16":
             # the same step through the shared-prefix path, groups from the manager
             gs, pb = m.prefix_groups(active)
@@ -223,7 +235,7 @@ def test_serving_loop_with_sharing_cow_and_swap(dt):
             pa.decode_shared_prefix(out2, _dev(q, dt), kd, vd, _i32(tables), _i32(lens),
                                     _i32(gs), _i32(pb), float(scale), bs)
             torch.cuda.synchronize()
-            assert float(np.abs(out2.cpu().numpy() - ref).max()) <= TOL[dt], step
+            _bars(float(np.abs(out2.cpu().numpy() - ref).max()), dt, step)
     assert np.array_equal(_raw(_np(hkd, dt)), _raw(hk))
     st_ = m.stats()
     # the full prompt blocks stay shared by the 6 that never left, and the two

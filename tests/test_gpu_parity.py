@@ -16,6 +16,18 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
+# The stated bars above, and a regression line far below them: the bf16
+# kernels carry the softmax weights to about 16 bits (a hi/lo pair of bf16
+# operands), so their error against the float64 oracle is ~1e-6; a change that
+# loses that precision fails here long before it reaches the bar.
+REGRESSION = {"f32": 1e-5, "bf16": 1e-4}
+
+
+def _bars(err, dt, *msg):
+    """Assert the stated bar and the regression line for KV dtype `dt`."""
+    assert err <= TOL[dt], (err, TOL[dt], *msg)
+    assert err <= REGRESSION[dt], ("above the regression line", err, REGRESSION[dt], *msg)
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -93,7 +105,7 @@ def test_parity_configs(case, poison):
     err = float(np.abs(out - ref).max())
     _say(f"  max-abs err {err:.3e} (tol {TOL[w.kv_dtype]:.0e})")
     assert np.isfinite(out).all()
-    assert err <= TOL[w.kv_dtype]
+    _bars(err, w.kv_dtype)
 
 
 def test_determinism_and_shuffle_invariance():
@@ -119,14 +131,14 @@ def test_partition_sizes_long_context(partition_tokens):
     out = _run(w, partition_tokens=partition_tokens).out.cpu().numpy()
     err = float(np.abs(out - ref).max())
     _say(f"  max-abs err {err:.3e}")
-    assert err <= TOL["bf16"]
+    _bars(err, "bf16")
 
 
 @pytest.mark.parametrize("partition_tokens", [0, 16, 64])
 def test_vector_alu_kernel_bf16(partition_tokens):
     w, _, _, ref = _case(cfg=2, num_seqs=6)
     out = _run(w, vector_alu=True, partition_tokens=partition_tokens).out.cpu().numpy()
-    assert float(np.abs(out - ref).max()) <= TOL["bf16"]
+    _bars(float(np.abs(out - ref).max()), "bf16")
 
 
 def _custom(lens, Hq, Hkv, D, bs, dtype, seed=0, poison="nan", num_blocks=None):
@@ -151,7 +163,7 @@ def test_edge_lengths_all_compiled_shapes(shape):
     ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, bs, dt)
     for pt in (0, bs, 4 * bs):
         out = _run(w, partition_tokens=pt).out.cpu().numpy()
-        assert np.abs(out - ref).max() <= TOL[dt], (pt, np.abs(out - ref).max())
+        _bars(np.abs(out - ref).max(), dt, (pt, np.abs(out - ref).max()))
         assert np.all(out[1] == 0.0)                          # L = 0
         G = Hq // Hkv
         for h in range(Hq):                                   # L = 1 returns V[0] exactly
@@ -286,7 +298,7 @@ def test_decode_step_empty_parts():
     torch.cuda.synchronize()
     k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
     ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, 16, "f32")
-    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL["f32"]
+    _bars(float(np.abs(d.out.cpu().numpy() - ref).max()), "f32")
     e = upload(w)
     q0 = torch.zeros((0,) + tuple(e.q.shape[1:]), dtype=e.q.dtype, device="cuda:0")
     out0 = torch.zeros((0,) + tuple(e.out.shape[1:]), dtype=torch.float32, device="cuda:0")
@@ -312,7 +324,7 @@ def test_many_sequences_past_the_planner_cache():
         out = _run(w, partition_tokens=pt).out.cpu().numpy()
         err = float(np.abs(out - ref).max())
         _say(f"  partition_tokens={pt} max-abs err {err:.3e}")
-        assert err <= TOL["bf16"]
+        _bars(err, "bf16")
         assert np.all(out[np.asarray(lens) == 0] == 0.0)
 
 
@@ -329,7 +341,7 @@ def test_claim_pools_with_other_cu_counts(cus, monkeypatch):
         err = float(np.abs(out - ref).max())
         _say(f"  max-abs err {err:.3e}")
         assert np.isfinite(out).all()
-        assert err <= TOL["bf16"]
+        _bars(err, "bf16")
 
 
 @pytest.mark.parametrize("grid", ["1", "3", "17", "40", "63", "100"])
@@ -349,7 +361,7 @@ def test_small_decode_grids(grid, monkeypatch):
         monkeypatch.delenv("PA_DECODE_GRID_OVERRIDE")
         err = float(np.abs(out - ref).max())
         _say(f"  max-abs err {err:.3e}")
-        assert err <= TOL["bf16"]
+        _bars(err, "bf16")
         assert np.array_equal(fixed.view(np.uint32), base.view(np.uint32))
 
 
@@ -372,7 +384,7 @@ def test_decode_check_on_a_caller_workspace():
                   float(w.scale), w.block_size, stream=side, workspace=ws)
     assert pa.decode_check(ws, stream=side) == 0
     torch.cuda.synchronize()
-    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL["bf16"]
+    _bars(float(np.abs(d.out.cpu().numpy() - ref).max()), "bf16")
 
 
 RANDOM_CASES = list(range(24))
@@ -406,7 +418,7 @@ def test_random_batches(seed):
     err = float(np.abs(out - ref).max()) if out.size else 0.0
     _say(f"  max-abs err {err:.3e}")
     assert np.isfinite(out).all()
-    assert err <= TOL[dt]
+    _bars(err, dt)
 
 
 def test_validate_option_rejects_before_launch():
@@ -421,7 +433,7 @@ def test_validate_option_rejects_before_launch():
     pa.decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(w.scale),
               w.block_size, validate=True)
     torch.cuda.synchronize()
-    assert float(np.abs(d.out.cpu().numpy() - ref).max()) <= TOL[w.kv_dtype]
+    _bars(float(np.abs(d.out.cpu().numpy() - ref).max()), w.kv_dtype)
     bad = d.block_tables.clone()
     s = int(np.argmax(w.context_lens))
     bad[s, 0] = w.num_blocks + 5
@@ -464,4 +476,4 @@ def test_decode_step_random_batches(seed):
     assert torch.equal(a.out.view(torch.int32), b.out.view(torch.int32))
     k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, bs)
     ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, bs, dt)
-    assert float(np.abs(b.out.cpu().numpy() - ref).max()) <= TOL[dt]
+    _bars(float(np.abs(b.out.cpu().numpy() - ref).max()), dt)

@@ -16,7 +16,13 @@ from paged_kv_cache_349_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
+TOL = 2e-2           # the stated bar for bf16 KV
+REGRESSION = 1e-4    # regression line: the kernels' error is ~1e-6 (16-bit softmax weights)
+
+
+def _bars(err, bound=1.0):
+    assert err <= TOL * bound, (err, TOL * bound)
+    assert err <= REGRESSION * bound, ("above the regression line", err, REGRESSION * bound)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -88,12 +94,12 @@ def test_parallel_sampling_workload(partition_tokens):
     out, d = _prefix_run(w, starts, pblocks, partition_tokens=partition_tokens)
     err = float(np.abs(out - ref).max())
     _say(f"  max-abs err {err:.2e}")
-    assert err <= TOL
+    _bars(err)
     # and against the plain kernel on the same inputs
     plain = torch.empty_like(d.out)
     pa.decode(plain, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(w.scale), 16)
     torch.cuda.synchronize()
-    assert float(np.abs(out - plain.cpu().numpy()).max()) <= 2 * TOL
+    _bars(float(np.abs(out - plain.cpu().numpy()).max()), 2)
 
 
 def _custom(lens, groups, prefix, Hq, Hkv, D, bs, seed):
@@ -137,7 +143,7 @@ def test_group_shapes(case):
     ref = _oracle(w)
     err = float(np.abs(out - ref).max())
     _say(f"  max-abs err {err:.2e}")
-    assert err <= TOL
+    _bars(err)
 
 
 def test_prefix_hint_clamped_and_empty_tail():
@@ -147,11 +153,11 @@ def test_prefix_hint_clamped_and_empty_tail():
     lens = np.array([64, 120, 140], np.int32)       # sequence 0 stops at the prefix
     out, _ = _prefix_run(w, [0, 3], [50], lens=lens)
     ref = _oracle(w, lens)
-    assert float(np.abs(out - ref).max()) <= TOL
+    _bars(float(np.abs(out - ref).max()))
     # a hint of 0 and no groups at all give plain decode results
     for starts, pb in (([0, 3], [0]), ([0], [])):
         out, _ = _prefix_run(w, starts, pb, lens=lens)
-        assert float(np.abs(out - ref).max()) <= TOL
+        _bars(float(np.abs(out - ref).max()))
 
 
 def test_unordered_groups_are_ignored():
@@ -163,7 +169,7 @@ def test_unordered_groups_are_ignored():
     ref = _oracle(w)
     bad, _ = _prefix_run(w, [0, S, 0, S], [12, 12, 12])
     none, _ = _prefix_run(w, [0], [])
-    assert float(np.abs(bad - ref).max()) <= TOL
+    _bars(float(np.abs(bad - ref).max()))
     assert np.array_equal(bad.view(np.uint32), none.view(np.uint32))
 
 
@@ -220,4 +226,4 @@ def test_random_groupings(seed):
     err = float(np.abs(out - ref).max())
     _say(f"  max-abs err {err:.2e}")
     assert np.isfinite(out).all()
-    assert err <= TOL
+    _bars(err)

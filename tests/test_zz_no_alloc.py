@@ -14,6 +14,18 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
+# The stated bars above, and a regression line far below them: the bf16
+# kernels carry the softmax weights to about 16 bits (a hi/lo pair of bf16
+# operands), so their error against the float64 oracle is ~1e-6; a change that
+# loses that precision fails here long before it reaches the bar.
+REGRESSION = {"f32": 1e-5, "bf16": 1e-4}
+
+
+def _bars(err, dt, *msg):
+    """Assert the stated bar and the regression line for KV dtype `dt`."""
+    assert err <= TOL[dt], (err, TOL[dt], *msg)
+    assert err <= REGRESSION[dt], ("above the regression line", err, REGRESSION[dt], *msg)
+
 
 def _say(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -57,13 +69,13 @@ def test_noalloc_matches_decode_two_calls_then_fp32():
     for w in cases:
         _say(f"no-alloc case {w.name} S={w.num_seqs}")
         plain, noalloc, ref = _both(w)
-        tol = TOL[w.kv_dtype]
         e_plain = float(np.abs(noalloc - plain).max())
         e_ref = float(np.abs(noalloc - ref).max())
         same = bool(np.array_equal(noalloc.view(np.uint32), plain.view(np.uint32)))
         _say(f"  vs pa_decode {e_plain:.3e} (bitwise {same}), vs oracle {e_ref:.3e}")
         assert np.isfinite(noalloc).all()
-        assert e_plain <= tol and e_ref <= tol
+        _bars(e_plain, w.kv_dtype)
+        _bars(e_ref, w.kv_dtype)
 
 
 def test_noalloc_rejects_oversized_shapes_before_launch():
