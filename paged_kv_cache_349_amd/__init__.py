@@ -23,7 +23,8 @@ import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "lib", "libpa.so")
+# PA_LIBRARY names another build of the library (e.g. the host sanitizer build).
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(PKG_DIR, "lib", "libpa.so")
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
