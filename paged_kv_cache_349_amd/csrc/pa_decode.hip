@@ -163,23 +163,26 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& a, int s, int block
 // Work list.
 // ---------------------------------------------------------------------------
 
-// Sum over each 16-lane row of a wave (every lane of the row gets it).
-__device__ __forceinline__ int row16_sum(int v) {
+// Sum over each run of NW lanes of a wave (every lane of the run gets it).
+template <int NW>
+__device__ __forceinline__ int lanes_sum(int v) {
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 1; off < NW; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-// Block-wide sum over the planner's 1024 threads (16 waves).  The 16 wave
+// Block-wide sum over the planner's NT threads (NT / 64 waves).  The wave
 // sums are read with one LDS load per lane and added across lanes, not by
-// 16 dependent loads.
-__device__ __forceinline__ int block_sum_1024(int v, int* scratch16) {
+// dependent loads.
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int* scratch) {
+  constexpr int NW = NT / 64;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch16[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
-  return row16_sum(scratch16[threadIdx.x & 15]);
+  return lanes_sum<NW>(scratch[threadIdx.x & (NW - 1)]);
 }
 
 constexpr int kPartChoices = 8;
@@ -285,12 +288,16 @@ __host__ __device__ __forceinline__ bool small_plan(const DecodeParams& a) {
 }
 
 
+// NT threads (256 or 1024: at least kTailClasses).
+template <int NT>
 __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size) {
+  static_assert(NT >= kTailClasses && NT % 64 == 0 && NT <= 1024, "planner width");
+  constexpr int NW = NT / 64;
   __shared__ int lens_c[kLensCached];
   __shared__ int start_c[kLensCached];   // shared-prefix blocks per sequence
   __shared__ int cls_off[kTailClasses];
   __shared__ int wave_sum[16];
-  __shared__ int chunk_incl[1024];
+  __shared__ int chunk_incl[NT];
   __shared__ int long_seen;
   __shared__ int run_base;
   __shared__ int nsplit;
@@ -301,7 +308,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   const int S = a.num_seqs;
   bool prefix = a.num_groups > 0;   // then S <= kLensCached (checked on the host)
 
-  for (int i = tid; i < kTailClasses; i += 1024) cls_off[i] = 0;
+  for (int i = tid; i < kTailClasses; i += NT) cls_off[i] = 0;
   if (tid == 0) {
     run_base = 0;
     long_seen = 0;
@@ -310,7 +317,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     npitems = 0;
     pitems_end = INT_MAX;
   }
-  // Group g's bounds and prefix hint, read by thread g (for the first 1024
+  // Group g's bounds and prefix hint, read by thread g (for the first NT
   // groups) together with the lengths, in one memory round trip.
   int reg_lo = 0, reg_hi = 0, reg_pb = 0;
   if (prefix && tid < a.num_groups) {
@@ -324,16 +331,16 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // ignored and the batch is decoded plainly (the same result).
   if (prefix) {
     int bad = 0;
-    for (int g = tid; g < a.num_groups; g += 1024) {
-      const int lo = g < 1024 ? reg_lo : a.group_starts[g];
-      const int hi = g < 1024 ? reg_hi : a.group_starts[g + 1];
+    for (int g = tid; g < a.num_groups; g += NT) {
+      const int lo = g < NT ? reg_lo : a.group_starts[g];
+      const int hi = g < NT ? reg_hi : a.group_starts[g + 1];
       bad |= hi < lo;
     }
-    prefix = block_sum_1024(bad, wave_sum) == 0;
+    prefix = block_sum<NT>(bad, wave_sum) == 0;
   }
   // One pass over the context lengths (clamped), kept in LDS for the passes
   // below.  S * max_blocks fits in int32 (checked on the host).
-  for (int s = tid; s < S; s += 1024) {
+  for (int s = tid; s < S; s += NT) {
     if (s < kLensCached) lens_c[s] = clamp_len(a, s, block_size);
     if (prefix) start_c[s] = 0;
   }
@@ -352,7 +359,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   int pre_mine = 0;
   const int num_groups = prefix ? a.num_groups : 0;
   if (prefix) {
-    for (int g = tid; g < num_groups; g += 1024) {
+    for (int g = tid; g < num_groups; g += NT) {
       int lo, hi;
       group_range(g, lo, hi);
       if (hi - lo < 2) continue;
@@ -365,11 +372,11 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     }
   }
   // (The sum's barriers also publish start_c.)
-  const int64_t pre_total = prefix ? block_sum_1024(pre_mine, wave_sum) : 0;
+  const int64_t pre_total = prefix ? block_sum<NT>(pre_mine, wave_sum) : 0;
   int mine = 0;
-  for (int s = tid; s < S; s += 1024)
+  for (int s = tid; s < S; s += NT)
     mine += (len_of(s) + block_size - 1) / block_size - start_of(s);
-  const int64_t total = block_sum_1024(mine, wave_sum);
+  const int64_t total = block_sum<NT>(mine, wave_sum);
 
   // Partition size (choose_part_blocks).  Long partitions mean few partition
   // states to merge; short ones spread a long context over many workgroups.
@@ -401,7 +408,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // item that zeroes its output); count partial partitions per class; list
   // the sequences whose states are merged: those spanning several partitions
   // and all that have a shared prefix (prefix partitions come first).
-  for (int c0 = 0; c0 < S; c0 += 1024) {
+  for (int c0 = 0; c0 < S; c0 += NT) {
     const int s = c0 + tid;
     int nfull = 0, L = 0, P = 0;
     if (s < S) {
@@ -428,9 +435,9 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     if (lane == 63) wave_sum[wave] = incl;
     if (nfull > kDirectItems) long_seen = 1;
     __syncthreads();
-    const int wsum = wave_sum[lane & 15];
-    const int chunk = row16_sum(wsum);
-    const int before = row16_sum((lane & 15) < wave ? wsum : 0);
+    const int wsum = wave_sum[lane & (NW - 1)];
+    const int chunk = lanes_sum<NW>(wsum);
+    const int before = lanes_sum<NW>((lane & (NW - 1)) < wave ? wsum : 0);
     // A sequence's first kDirectItems full partitions are listed by its own
     // thread.  Any further ones (long contexts) are listed by all threads,
     // each finding its sequence by binary search over the chunk's inclusive
@@ -440,8 +447,8 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
     chunk_incl[tid] = before + incl;
     __syncthreads();
     if (long_seen) {
-      for (int i = tid; i < chunk; i += 1024) {
-        int lo = 0, hi = min(S - c0, 1024) - 1;
+      for (int i = tid; i < chunk; i += NT) {
+        int lo = 0, hi = min(S - c0, NT) - 1;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (chunk_incl[mid] > i) hi = mid; else lo = mid + 1;
@@ -487,7 +494,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 
   // Pass 2: partial partitions.  The order inside a class is arbitrary; it
   // changes which workgroup computes an item, never the result.
-  for (int s = tid; s < S; s += 1024) {
+  for (int s = tid; s < S; s += NT) {
     const int L = len_of(s);
     const int P = start_of(s);
     const int nblk = (L + block_size - 1) / block_size - P;
@@ -503,7 +510,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // so that no input can make the planner write past the list.
   if (prefix) {
     const int64_t cap = (int64_t)S * a.num_parts_max;
-    for (int g = tid; g < num_groups; g += 1024) {
+    for (int g = tid; g < num_groups; g += NT) {
       int lo, hi;
       group_range(g, lo, hi);
       if (hi - lo < 2) continue;
@@ -531,13 +538,15 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 // others (the step's write and plan are independent, so they share a launch).
 // The block size is a template parameter so that the planner's divisions by
 // it are shifts.
-template <int BS>
-__global__ __launch_bounds__(1024) void plan_items(DecodeParams a) {
-  if (small_plan(a)) {
-    if (threadIdx.x < 64) plan_small<BS>(a);   // launched with one wave for such batches
-    return;
+// NT threads: one wave for batches plan_small plans, 256 for up to 256
+// sequences, else 1024 (chosen by launch_decode_shape).
+template <int BS, int NT>
+__global__ __launch_bounds__(NT) void plan_items(DecodeParams a) {
+  if constexpr (NT == 64) {
+    plan_small<BS>(a);
+  } else {
+    plan_body<NT>(a, BS);
   }
-  plan_body(a, BS);
 }
 
 template <typename E, int BS>
@@ -547,7 +556,7 @@ __global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, WriteArgs
       if (threadIdx.x < 64) plan_small<BS>(a);
       return;
     }
-    plan_body(a, BS);
+    plan_body<1024>(a, BS);
     return;
   }
   write_elements<E>(w, (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x,
@@ -1838,7 +1847,12 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
     else
       hipLaunchKernelGGL((write_and_plan<uint32_t, BS>), grid, dim3(1024), 0, stream, p, *write);
   } else {
-    hipLaunchKernelGGL(plan_items<BS>, dim3(1), dim3(small_plan(p) ? 64 : 1024), 0, stream, p);
+    if (small_plan(p))
+      hipLaunchKernelGGL((plan_items<BS, 64>), dim3(1), dim3(64), 0, stream, p);
+    else if (p.num_seqs <= 256)
+      hipLaunchKernelGGL((plan_items<BS, 256>), dim3(1), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((plan_items<BS, 1024>), dim3(1), dim3(1024), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
