@@ -1144,14 +1144,20 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     Desc d;
     const int item = item_for(r);
     d.valid = item < total;
-    const int e_idx = d.valid ? item / Hkv : 0;
-    d.s = items[4 * e_idx + 0];
-    d.part = items[4 * e_idx + 1];
-    d.L = d.valid ? items[4 * e_idx + 2] : 0;
+    // The entry is read before `total` is known (its address does not depend
+    // on it), so the first item's list entry and the control words arrive in
+    // one memory round trip: round 0's item is the workgroup's index, below
+    // the list's capacity.  Fields of an item past the end are not used.
+    const int e_idx = min(item / Hkv, a.num_seqs * a.num_parts_max - 1);
+    const int e_s = items[4 * e_idx + 0], e_part = items[4 * e_idx + 1];
+    const int e_L = items[4 * e_idx + 2], e_P = items[4 * e_idx + 3];
+    d.s = d.valid ? e_s : 0;
+    d.part = d.valid ? e_part : 0;
+    d.L = d.valid ? e_L : 0;
     d.h = d.valid ? item - e_idx * Hkv : 0;
     // Blocks before P belong to the sequence's shared prefix, computed by
     // the prefix kernel as the first partition states of the sequence.
-    const int P = d.valid ? items[4 * e_idx + 3] : 0;
+    const int P = d.valid ? e_P : 0;
     const int nblk = (d.L + BS - 1) / BS;
     d.b0 = P + d.part * pb;
     const int nb = min(d.b0 + pb, nblk) - d.b0;
