@@ -1588,19 +1588,20 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 //   once and merges them alone, with no barrier.  Unit u goes to workgroup
 //   u % grid, row (u / grid) % R of its R = threads / C rows of C columns:
 //   units spread over all workgroups before any takes a second one.
-//   Long units: one workgroup per unit, the last workgroups first.  Wave
-//   g % kMergeWaves finds M and lambda of head g over lane-strided
-//   partitions; rows of threads take
-//   contiguous runs of partitions of one column for the weighted sum, whose
-//   terms do not depend on one another, and the rows' partial sums are added
-//   in row order.  A unit's first loads (kMergeBatch partitions per row,
-//   kMergeHeld * 64 (m, l) pairs per head) are issued before any reduction.
+//   Long units: one workgroup per (unit, query head), the last workgroups
+//   first, so the G heads of a long sequence's unit are merged by G
+//   workgroups at once.  The head's M and lambda come from all threads over
+//   thread-strided partitions; rows of threads take contiguous runs of
+//   partitions of one column for the weighted sum, whose terms do not depend
+//   on one another, and the rows' partial sums are added in row order.  A
+//   row's first kMergeBatch partitions are loaded before the reductions.
+//   (One workgroup per unit, all heads together: the skewed long-context
+//   workload's merge of a 128-partition sequence took 7.7 us per call.)
 // Every order depends only on the partition count, so results are
 // reproducible.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = 64 * kMergeWaves;
 constexpr int kMergeBatch = 32;
-constexpr int kMergeHeld = 2;
 constexpr int kMergeGrid = 256;
 static_assert(kMergeShort <= kMergeBatch, "a short unit's partitions are loaded in one batch");
 
@@ -1608,7 +1609,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
   constexpr int kCols4 = D / 4;
-  __shared__ float head_max[kMaxGroup], head_sum[kMaxGroup];
+  __shared__ float head_max[kMergeWaves], head_sum[kMergeWaves];
   __shared__ f4 partial[kMergeThreads];
   const int Hkv = a.num_kv_heads, G = a.group, S = a.num_seqs;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1654,71 +1655,63 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     }
   }
 
-  for (int64_t u = gridDim.x - 1 - blockIdx.x; u < n_long; u += gridDim.x) {
-    const int2 e = a.ws_split[S - 1 - u / Hkv];
-    const int h = (int)(u % Hkv);
+  // Long units, one query head per workgroup (so a long sequence's partition
+  // states are read by G workgroups at once, not one): unit u is (split
+  // sequence u / (Hkv * G), KV head, query head u % G).  The head's maximum
+  // and sum come first (thread t takes partitions t, t + threads, ...), then
+  // rows of kCols4 threads take contiguous runs of partitions of one column
+  // each, and the rows' partial sums are added in row order.
+  constexpr int kRowsH = kMergeThreads / kCols4;
+  const int rh = tid / kCols4, ch = tid - rh * kCols4;
+  for (int64_t u = gridDim.x - 1 - blockIdx.x; u < n_long * G; u += gridDim.x) {
+    const int64_t uh = u / G;                  // (split sequence, KV head)
+    const int gq = (int)(u - uh * G);
+    const int2 e = a.ws_split[S - 1 - uh / Hkv];
+    const int h = (int)(uh % Hkv);
     const int s = e.x, nparts = e.y;
     const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
-    const int p_lo = (int)((int64_t)nparts * r / R), p_hi = (int)((int64_t)nparts * (r + 1) / R);
-    const bool sums = r < R;
+    const int p_lo = (int)((int64_t)nparts * rh / kRowsH);
+    const int p_hi = (int)((int64_t)nparts * (rh + 1) / kRowsH);
+    // This row's first batch of weighted sums, in flight during the reductions.
     float mp[kMergeBatch];
     f4 ap[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int64_t row = (prow + max(min(min(p_lo + j, p_hi - 1), nparts - 1), 0)) * G + g;
-      mp[j] = sums && p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
-      ap[j] = sums && p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
-                                      : f4{0.f, 0.f, 0.f, 0.f};
+      const int64_t row = (prow + max(min(p_lo + j, p_hi - 1), 0)) * G + gq;
+      mp[j] = p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
+      ap[j] = p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4)
+                              : f4{0.f, 0.f, 0.f, 0.f};
     }
-    float2 held[kMergeHeld];
-    const int g1 = wave < G ? wave : 0;
+    float m = kNegInf;
+    for (int p = tid; p < nparts; p += kMergeThreads) m = fmaxf(m, ml[(prow + p) * G + gq].x);
 #pragma unroll
-    for (int j = 0; j < kMergeHeld; ++j) {
-      const int p = lane + 64 * j;
-      held[j] = wave < G && p < nparts ? ml[(prow + p) * G + g1] : make_float2(kNegInf, 0.f);
-    }
-    for (int gg = wave; gg < G; gg += kMergeWaves) {
-      float m = kNegInf;
-      if (gg == wave) {
-#pragma unroll
-        for (int j = 0; j < kMergeHeld; ++j) m = fmaxf(m, held[j].x);
-      }
-      for (int p = lane + (gg == wave ? 64 * kMergeHeld : 0); p < nparts; p += 64)
-        m = fmaxf(m, ml[(prow + p) * G + gg].x);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
-      float l = 0.f;
-      if (m != kNegInf) {
-        if (gg == wave) {
-#pragma unroll
-          for (int j = 0; j < kMergeHeld; ++j)
-            if (held[j].x != kNegInf) l += held[j].y * exp2_fast(held[j].x - m);
-        }
-        for (int p = lane + (gg == wave ? 64 * kMergeHeld : 0); p < nparts; p += 64) {
-          const float2 v = ml[(prow + p) * G + gg];
-          if (v.x != kNegInf) l += v.y * exp2_fast(v.x - m);
-        }
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) l += shfl_xor_f(l, off);
-      if (lane == 0) {
-        head_max[gg] = m;
-        head_sum[gg] = l;
-      }
-    }
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+    if (lane == 0) head_max[wave] = m;
     __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < kMergeWaves; ++v) M = fmaxf(M, head_max[v]);
+    float l = 0.f;
+    if (M != kNegInf) {
+      for (int p = tid; p < nparts; p += kMergeThreads) {
+        const float2 v = ml[(prow + p) * G + gq];
+        if (v.x != kNegInf) l += v.y * exp2_fast(v.x - M);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l += shfl_xor_f(l, off);
+    if (lane == 0) head_sum[wave] = l;
     f4 val = {0.f, 0.f, 0.f, 0.f};
-    if (sums && head_max[g] != kNegInf) {
-      const float M = head_max[g];
+    if (M != kNegInf) {
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j)
         if (mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
       for (int p0 = p_lo + kMergeBatch; p0 < p_hi; p0 += kMergeBatch) {
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-          const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + g;
+          const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + gq;
           mp[j] = a.ws_ml[row * 2];
-          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
+          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
         }
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j)
@@ -1727,11 +1720,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     }
     partial[tid] = val;
     __syncthreads();
-    if (tid < C) {
+    if (tid < kCols4) {
       f4 sum = partial[tid];
-      for (int rr = 1; rr < R; ++rr) sum += partial[rr * C + tid];
-      const float lam = head_sum[g];
-      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + g) * D + d4 * 4) =
+      for (int rr = 1; rr < kRowsH; ++rr) sum += partial[rr * kCols4 + tid];
+      float lam = 0.f;
+#pragma unroll
+      for (int v = 0; v < kMergeWaves; ++v) lam += head_sum[v];
+      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + gq) * D + tid * 4) =
           lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();   // head_max, head_sum and partial are reused by the next unit
@@ -1879,12 +1874,12 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
   if (p.num_parts_max <= 1) return hipSuccess;
-  // One workgroup per (sequence, KV head) of a batch whose every sequence is
-  // split, up to kMergeGrid; the kernel loops past that.  Only the planner
+  // One workgroup per (sequence, KV head, query head) of a batch whose every
+  // sequence is split, up to kMergeGrid; the kernel loops past that.  Only the planner
   // knows how many sequences are split; a workgroup beyond that count still
   // occupies its wave slots for a memory round trip before it exits, so the
   // grid is kept small.
-  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * p.group;
   const unsigned mgrid = (unsigned)(units < kMergeGrid ? units : kMergeGrid);
   hipLaunchKernelGGL(merge_splits<D>, dim3(mgrid), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
