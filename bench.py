@@ -489,7 +489,7 @@ def parse_args():
                    help="skip the shared-prefix decode measurement (parallel-sampling workload)")
     p.add_argument("--configs", default="2,3,4",
                    help="comma-separated other workloads measured cold in the `configs` record "
-                        "('' = none)")
+                        "('none' = no record)")
     p.add_argument("--config-iters", type=int, default=20,
                    help="cold launches per measurement in the `configs` record")
     p.add_argument("--configs-only", action="store_true",
@@ -524,7 +524,8 @@ def main() -> int:
     pa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    which = [int(c) for c in args.configs.split(",") if c.strip()]
+    which = [] if args.configs.strip().lower() in ("", "none") else \
+        [int(c) for c in args.configs.split(",") if c.strip()]
     if args.configs_only:
         res = bench_configs(args, dev, torch.cuda.current_stream(dev), which)
         print(json.dumps({"configs": res}), flush=True)
