@@ -709,6 +709,23 @@ def main() -> int:
         ck_ms, ck_n = pa.kernel_timing_end()
         contig_kern = ck_ms * 1e3 / ck_n
         out_c = dc.out.cpu().numpy()
+        # The packed pool once more without per-block table reads (block j of
+        # sequence s = its first table entry + j): splits the paged cost into
+        # the table reads and the scatter of blocks over the pool.
+        def decode_packed():
+            pa.decode(dc.out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                      float(wc.scale), wc.block_size, partition_tokens=args.partition_tokens,
+                      packed_pool=True)
+        packed_kern = None
+        if not args.shared_prefix and wc.kv_dtype == "bf16":
+            for _ in range(args.warmup):
+                decode_packed()
+            pa.kernel_timing_begin(K)
+            for i in range(K):
+                decode_packed()
+            torch.cuda.synchronize()
+            pk_ms, pk_n = pa.kernel_timing_end()
+            packed_kern = pk_ms * 1e3 / pk_n
         decode()
         torch.cuda.synchronize()
         result["paged_decode_us_mean"] = round(paged_us, 2)
@@ -718,6 +735,15 @@ def main() -> int:
         result["paged_overhead_vs_contig_kernel"] = round(kern_mean / contig_kern - 1.0, 4)
         result["contig_output_bitwise_equal"] = bool(
             np.array_equal(out_c.view(np.uint32), d.out.cpu().numpy().view(np.uint32)))
+        if packed_kern is not None:
+            result["packed_no_table_kernel_us_mean"] = round(packed_kern, 2)
+            result["paged_cost_split_kernel"] = {
+                "table_reads": round(contig_kern / packed_kern - 1.0, 4),
+                "block_scatter": round(kern_mean / contig_kern - 1.0, 4),
+            }
+            log(f"attention kernel on the packed pool without per-block table reads "
+                f"{packed_kern:.1f} us: table reads {contig_kern / packed_kern - 1:.2%}, "
+                f"scatter {kern_mean / contig_kern - 1:.2%}")
         log(f"decode call paged {paged_us:.1f} us, contiguous {contig_us:.1f} us "
             f"(overhead {paged_us / contig_us - 1:.2%}); attention kernel paged {kern_mean:.1f} us, "
             f"contiguous {contig_kern:.1f} us (overhead {kern_mean / contig_kern - 1:.2%})")

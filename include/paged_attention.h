@@ -200,10 +200,18 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
  * partition_tokens: tokens handled by one workgroup (a multiple of
  * block_size, or 0 for the library's choice).  flags: PA_FLAG_VECTOR_ALU
  * selects the plain vector-ALU kernel also for bf16 (by default bf16 uses the
- * matrix-core kernel).  The workspace must hold
+ * matrix-core kernel).  PA_FLAG_PACKED_POOL is a diagnostic for a pool that
+ * holds each sequence's blocks consecutively: block j of sequence s is taken
+ * to be block_tables[s, 0] + j, and only the first entry of each row is read
+ * (bf16 matrix-core kernel only; else PA_ERR_UNSUPPORTED).  On such a pool it
+ * gives the same bits as the ordinary path; timing the two on one packed pool
+ * isolates the cost of reading the table per block ("PagedAttention and KV
+ * memory management", section "Myths and failure modes": the indirection
+ * costs a few percent).  The workspace must hold
  * pa_decode_workspace_bytes_ex(..., partition_tokens) bytes.
  */
 #define PA_FLAG_VECTOR_ALU 1
+#define PA_FLAG_PACKED_POOL 2
 int pa_decode_ex(float* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* context_lens, float scale,
                  int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

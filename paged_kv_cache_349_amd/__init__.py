@@ -29,6 +29,7 @@ LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(PKG_DIR, "lib", "libpa.s
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_FLAG_VECTOR_ALU = 1
+PA_FLAG_PACKED_POOL = 2
 
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_WORKSPACE",
            4: "PA_ERR_LAUNCH"}
@@ -331,10 +332,13 @@ def decode_check(workspace=None, stream=None, device=None, *, noalloc=False) -> 
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None,
-           *, workspace=None, partition_tokens=0, vector_alu=False, validate=False):
+           *, workspace=None, partition_tokens=0, vector_alu=False, packed_pool=False,
+           validate=False):
     """Single-query attention per sequence over the paged KV pool; writes `out`.
     validate=True (or PA_VALIDATE=1) first checks the tables and lengths on the
-    host, which synchronises: for debugging."""
+    host, which synchronises: for debugging.  packed_pool=True is a diagnostic
+    for a pool whose sequences' blocks are consecutive (block j of sequence s =
+    block_tables[s, 0] + j; only the first entry of each row is read)."""
     torch = _torch()
     lib = load_library()
     dev = _on_gpu(out, q, k_cache, v_cache, block_tables, context_lens)
@@ -360,7 +364,7 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
         workspace = _workspace(dev, st, need)
     ws_ptr = workspace.data_ptr()
     ws_len = workspace.numel() * workspace.element_size()
-    flags = PA_FLAG_VECTOR_ALU if vector_alu else 0
+    flags = (PA_FLAG_VECTOR_ALU if vector_alu else 0) | (PA_FLAG_PACKED_POOL if packed_pool else 0)
     _check(lib.pa_decode_ex(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), context_lens.data_ptr(), float(scale), bs, S,
                             Hq, Hkv, D, max_blocks, NB, code, ws_ptr, ws_len, partition_tokens,

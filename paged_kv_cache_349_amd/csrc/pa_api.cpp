@@ -160,7 +160,12 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
     return fail(PA_ERR_INVALID_ARG, "num_heads=%d is not a multiple of num_kv_heads=%d",
                 num_heads, num_kv_heads);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  if (flags & ~PA_FLAG_VECTOR_ALU) return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(PA_FLAG_VECTOR_ALU | PA_FLAG_PACKED_POOL))
+    return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if ((flags & PA_FLAG_PACKED_POOL) &&
+      (kv_dtype != PA_DTYPE_BF16 || (flags & PA_FLAG_VECTOR_ALU) || prefix))
+    return fail(PA_ERR_UNSUPPORTED,
+                "the packed-pool diagnostic runs the bf16 matrix-core kernel without prefixes only");
   const int32_t group = num_heads / num_kv_heads;
   if (!pa::decode_supported((pa::KvType)kv_dtype, head_dim, block_size, group))
     return fail(PA_ERR_UNSUPPORTED,
@@ -235,6 +240,7 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
   p.num_groups = prefix ? num_groups : 0;
   p.prefix_rows = 0;   // set by the launcher
   p.ws_pitems = prefix ? (int4*)(ws + lay.pitems_off) : nullptr;
+  p.packed_pool = (flags & PA_FLAG_PACKED_POOL) ? 1 : 0;
   const auto ev = next_timing_events();
   hipError_t e = pa::launch_decode(p, sizeof(pa::DecodeParams), (pa::KvType)kv_dtype, head_dim,
                                    block_size, (flags & PA_FLAG_VECTOR_ALU) != 0,

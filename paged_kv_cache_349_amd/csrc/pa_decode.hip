@@ -977,6 +977,7 @@ __device__ __forceinline__ void prefix_items(const DecodeParams& a, float* smem,
 // One work item as a wave sees it (every field is uniform across the wave).
 struct Desc {
   int s, h, L, b0, nparts, part;
+  int base;         // packed-pool diagnostic: the sequence's first block id
   int wr;           // the wave's lane in the item: (w + round) mod W
   int nmine;        // the wave's 16-token positions in the item: wr, wr + W, ...
   int npos;         // positions the wave spends on the item: max(nmine, 1)
@@ -994,7 +995,12 @@ struct Desc {
 // them and wait only for the buffer it uses.  After the last position of an
 // item each wave hands its state to the item's LDS slot; the last wave of
 // the workgroup to do so merges them and writes the result (see finish).
-template <int D, int BS, int W, bool PREFIX>
+// TABLE = false is a diagnostic instantiation for a pool packed sequence by
+// sequence (block j of sequence s is block_tables[s, 0] + j): it reads one
+// table entry per item instead of one per block, so comparing it with the
+// ordinary kernel on the same packed pool isolates the cost of the per-block
+// table reads from that of blocks scattered over the pool.
+template <int D, int BS, int W, bool PREFIX, bool TABLE = true>
 __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
@@ -1158,6 +1164,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     // Blocks before P belong to the sequence's shared prefix, computed by
     // the prefix kernel as the first partition states of the sequence.
     const int P = d.valid ? e_P : 0;
+    d.base = !TABLE && d.valid && d.L > 0 ? tables[(int64_t)d.s * a.max_blocks] : 0;
     const int nblk = (d.L + BS - 1) / BS;
     d.b0 = P + d.part * pb;
     const int nb = min(d.b0 + pb, nblk) - d.b0;
@@ -1213,7 +1220,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     const int q = d.wr + k * W;
     const int kk = q / kHalves, half = q - kk * kHalves;
     int id = 0;
-    if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + kk];
+    if constexpr (TABLE) {
+      if (d.valid && k < d.nmine) id = tables[(int64_t)d.s * a.max_blocks + d.b0 + kk];
+    } else {
+      id = d.base + d.b0 + kk;
+    }
     has = d.valid && k < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
     const int64_t off = has ? ((int64_t)id * Hkv + d.h) * tile_bytes : 0;
     const uint32_t nb = has ? tile_bytes : 0;
@@ -1811,9 +1822,11 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   // share, so each wave's part of it is at most half a wave's share.
   if (p.balance) p.balance = kWaves / 2;
   const bool prefix = p.num_groups > 0;   // bf16 matrix-core kernel only (checked by the API)
+  const bool packed = p.packed_pool != 0;  // bf16 matrix-core kernel, no prefixes (checked by the API)
   if (type == KvType::BF16 && !vector_alu) {
     kernel = prefix ? (const void*)decode_mfma_bf16<D, BS, kWaves, true>
-                    : (const void*)decode_mfma_bf16<D, BS, kWaves, false>;
+                    : packed ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, false>
+                             : (const void*)decode_mfma_bf16<D, BS, kWaves, false>;
     smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
     if (prefix) {
       const size_t pre = (size_t)prefix_lds_floats<D, kWaves>() * 4;
@@ -1860,6 +1873,9 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
   if (type == KvType::BF16 && !vector_alu && prefix)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, true>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else if (type == KvType::BF16 && !vector_alu && packed)
+    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false, false>), dim3(p.decode_grid),
                        dim3(threads), smem, stream, p);
   else if (type == KvType::BF16 && !vector_alu)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false>), dim3(p.decode_grid),

@@ -49,6 +49,7 @@ struct DecodeParams {
   int32_t prefix_rows;          // query rows one prefix item serves (its sequences x group)
   int4* ws_pitems;              // [S * num_parts_max] prefix work list:
                                 //  (first sequence, sequences, partition, prefix blocks)
+  int32_t packed_pool;          // diagnostic: block j of sequence s is tables[s, 0] + j
 };
 
 // ws_ctrl slots written by the planner: work-list entries, chosen partition

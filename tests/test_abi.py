@@ -99,6 +99,9 @@ def _decode(lib, **kw):
     (dict(maxb=0), 1),
     (dict(scale=float("nan")), 1),
     (dict(flags=8), 1),
+    (dict(flags=4), 1),
+    (dict(flags=2, dt=0), 2),            # packed-pool diagnostic: bf16 matrix-core kernel only
+    (dict(flags=3), 2),
     (dict(pt=24), 1),
     (dict(out=None), 1),
     (dict(t=None), 1),

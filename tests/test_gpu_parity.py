@@ -387,6 +387,34 @@ def test_decode_check_on_a_caller_workspace():
     _bars(float(np.abs(d.out.cpu().numpy() - ref).max()), "bf16")
 
 
+@pytest.mark.parametrize("cfg,bs", [(2, 16), (5, 16), (5, 32), (3, 16)])
+def test_packed_pool_diagnostic(cfg, bs):
+    """The packed-pool diagnostic (block j of sequence s = block_tables[s, 0] + j,
+    one table entry read per item) gives the ordinary path's bits on a pool packed
+    sequence by sequence, and both match the oracle."""
+    import torch
+    import paged_kv_cache_349_amd as pa
+    from paged_kv_cache_349_amd.device_io import upload
+    w, _, _, ref = _case(cfg=cfg, block_size=bs if bs != 16 else None)
+    wc = wl.to_contiguous(w)
+    assert all(np.array_equal(wc.block_tables[s, :n], wc.block_tables[s, 0] + np.arange(n))
+               for s, n in enumerate(wc.blocks_per_seq()))
+    d = upload(wc)
+    pa.write_kv(d.k_cache, d.v_cache, d.k_new, d.v_new, d.slot_mapping)
+    outs = []
+    for packed in (False, True):
+        out = torch.full_like(d.out, float("nan"))
+        pa.decode(out, d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(w.scale),
+                  w.block_size, packed_pool=packed)
+        outs.append(out)
+    torch.cuda.synchronize()
+    _assert_no_abort()
+    a, b = outs[0].cpu().numpy(), outs[1].cpu().numpy()
+    _say(f"packed pool {w.name}: bitwise {np.array_equal(a.view(np.uint32), b.view(np.uint32))}")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    _bars(float(np.abs(b - ref).max()), w.kv_dtype)
+
+
 RANDOM_CASES = list(range(24))
 
 
