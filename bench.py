@@ -678,6 +678,7 @@ def main() -> int:
             cold.append(a.elapsed_time(b) * 1e3)
         del flush
         result["decode_us_cold_median"] = round(statistics.median(cold), 2)
+        result["decode_us_cold_p10_p90"] = [round(float(x), 2) for x in np.percentile(cold, [10, 90])]
         log(f"cold decode median {statistics.median(cold):.1f} us")
 
     if not args.no_contig:

@@ -353,8 +353,12 @@ int pa_probe_read_tiles(const void* k_cache, const void* v_cache, const int32_t*
                         int32_t num_tiles, int32_t tile_bytes, int64_t pool_tiles, uint32_t* sink,
                         void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code.  pa_status_str is the same function
+ * under a shorter name.  Status and dtype arguments are int32_t rather than
+ * the enum types above, so that their size in the ABI is fixed; their values
+ * are the enumerators. */
 const char* pa_status_string(int32_t status);
+const char* pa_status_str(int32_t status);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char* pa_last_error(void);

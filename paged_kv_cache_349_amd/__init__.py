@@ -65,6 +65,7 @@ _SIGNATURES = {
     "pa_kernel_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(_c_int)]),
     "pa_status_string": (ctypes.c_char_p, [_c_int]),
+    "pa_status_str": (ctypes.c_char_p, [_c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
 }
 

@@ -291,6 +291,8 @@ const char* pa_status_string(int32_t status) {
   }
 }
 
+const char* pa_status_str(int32_t status) { return pa_status_string(status); }
+
 const char* pa_last_error(void) { return g_last_error; }
 
 // Argument checks of a slot write; PA_OK means it may be launched (a write

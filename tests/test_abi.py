@@ -50,6 +50,7 @@ def test_status_strings(lib):
     for code in range(5):
         assert lib.pa_status_string(code)
     assert lib.pa_status_string(99) == b"unknown status"
+    assert lib.pa_status_str(3) == lib.pa_status_string(3)
 
 
 def _align(n):
