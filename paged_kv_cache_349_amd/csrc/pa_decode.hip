@@ -163,26 +163,95 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& a, int s, int block
 // Work list.
 // ---------------------------------------------------------------------------
 
-// Sum over each run of NW lanes of a wave (every lane of the run gets it).
-template <int NW>
-__device__ __forceinline__ int lanes_sum(int v) {
-#pragma unroll
-  for (int off = 1; off < NW; off <<= 1) v += __shfl_xor(v, off, 64);
+// Cross-lane steps of the planners, through DPP: the operand of an ALU
+// instruction is read from another lane of the wave, with no trip through
+// LDS.  (ds_bpermute, which the generic shuffles use, goes through the LDS
+// pipeline, and the planners' 4 to 16 waves queue on it.)  Controls (GFX9):
+// row_shr:n, lane i of a 16-lane row reads lane i - n of the row; row_ror:n,
+// lane i reads lane (i - n) mod 16 of the row; wave_shr:1 / wave_shl:1, lane
+// i reads lane i - 1 / i + 1; row_bcast:15, every lane of a row reads lane 15
+// of the row before; row_bcast:31, every lane reads lane 31.  A lane whose
+// source is outside its range, or whose row is left out by ROWS, gets `id`.
+constexpr int kDppRowShr = 0x110;     // + n, 1 <= n <= 15
+constexpr int kDppRowRor = 0x120;     // + n, 1 <= n <= 15
+constexpr int kDppWaveShl1 = 0x130;
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_read(int id, int v) {
+  return __builtin_amdgcn_update_dpp(id, v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes with an associative, commutative `op`
+// whose identity is `id`: doubling shifts inside each row, then row 0's total
+// into row 1 and row 2's into row 3, then rows 0-1's total into rows 2-3.
+template <typename Op>
+__device__ __forceinline__ int wave_scan(int v, int id, Op op) {
+  v = op(v, dpp_read<kDppRowShr + 1>(id, v));
+  v = op(v, dpp_read<kDppRowShr + 2>(id, v));
+  v = op(v, dpp_read<kDppRowShr + 4>(id, v));
+  v = op(v, dpp_read<kDppRowShr + 8>(id, v));
+  v = op(v, dpp_read<kDppRowBcast15, 0xa>(id, v));
+  v = op(v, dpp_read<kDppRowBcast31, 0xc>(id, v));
   return v;
 }
 
-// Block-wide sum over the planner's NT threads (NT / 64 waves).  The wave
-// sums are read with one LDS load per lane and added across lanes, not by
-// dependent loads.
-template <int NT>
-__device__ __forceinline__ int block_sum(int v, int* scratch) {
-  constexpr int NW = NT / 64;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return lanes_sum<NW>(scratch[threadIdx.x & (NW - 1)]);
+struct AddOp {
+  __device__ int operator()(int a, int b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ int operator()(int a, int b) const { return max(a, b); }
+};
+
+__device__ __forceinline__ int wave_scan_sum(int v) { return wave_scan(v, 0, AddOp()); }
+__device__ __forceinline__ int wave_scan_max(int v) { return wave_scan(v, INT_MIN, MaxOp()); }
+
+// Sum over a wave (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_sum(v), 63);
+}
+
+// `op` over each run of NW lanes (NW a power of two, at most 16) of a value
+// that repeats every NW lanes; every lane gets the result.  Rotations inside
+// a row: after the step by n, each lane holds op over 2n consecutive lanes.
+template <int NW, typename Op>
+__device__ __forceinline__ int lanes_reduce(int v, Op op) {
+  static_assert(NW >= 1 && NW <= 16 && (NW & (NW - 1)) == 0, "lanes_reduce width");
+  if constexpr (NW >= 2) v = op(v, dpp_read<kDppRowRor + 1>(0, v));
+  if constexpr (NW >= 4) v = op(v, dpp_read<kDppRowRor + 2>(0, v));
+  if constexpr (NW >= 8) v = op(v, dpp_read<kDppRowRor + 4>(0, v));
+  if constexpr (NW >= 16) v = op(v, dpp_read<kDppRowRor + 8>(0, v));
+  return v;
+}
+
+// Sum over each run of NW lanes of a wave (the value repeats every NW lanes).
+template <int NW>
+__device__ __forceinline__ int lanes_sum(int v) {
+  return lanes_reduce<NW>(v, AddOp());
+}
+
+// Inclusive minimum over segments of adjacent lanes with equal `key` (no key
+// may recur after another one); the segment's last lane holds its minimum.
+// The scan of wave_scan, each step taken only from a lane of the segment:
+// with segments contiguous, a source lane with the same key has only lanes
+// of the segment between it and this lane.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int segment_step(int v, int key) {
+  const int sv = dpp_read<CTRL, ROWS>(INT_MAX, v);
+  const int sk = dpp_read<CTRL, ROWS>(INT_MIN, key);
+  return sk == key ? min(v, sv) : v;
+}
+
+__device__ __forceinline__ int segment_min(int v, int key) {
+  v = segment_step<kDppRowShr + 1>(v, key);
+  v = segment_step<kDppRowShr + 2>(v, key);
+  v = segment_step<kDppRowShr + 4>(v, key);
+  v = segment_step<kDppRowShr + 8>(v, key);
+  v = segment_step<kDppRowBcast15, 0xa>(v, key);
+  v = segment_step<kDppRowBcast31, 0xc>(v, key);
+  return v;
 }
 
 constexpr int kPartChoices = 8;
@@ -204,13 +273,6 @@ __device__ __forceinline__ int choose_part_blocks(const DecodeParams& a, int64_t
   return pb;
 }
 
-// Sum over a wave (every lane gets it).
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // The planner of a batch of at most 64 sequences without shared prefixes, in
 // one wave with no barrier: lane s plans sequence s.  Its lists are those of
 // plan_body (same partition size, same items, same split sequences) except
@@ -230,14 +292,9 @@ __device__ __forceinline__ void plan_small(const DecodeParams& a) {
   // zeroes its output); a sequence's first kDirectItems are listed by its
   // lane, any further ones by all lanes together.
   const int nfull = live ? (nblk == 0 ? 1 : nblk / pb) : 0;
-  int incl = nfull;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_scan_sum(nfull);
   const int base = incl - nfull;
-  const int n_full = __shfl(incl, 63, 64);
+  const int n_full = __builtin_amdgcn_readlane(incl, 63);
   for (int p = 0; p < min(nfull, kDirectItems); ++p)
     a.ws_items[base + p] = make_int4(lane, p, L, 0);
   if (__builtin_amdgcn_ballot_w64(nfull > kDirectItems)) {
@@ -288,13 +345,35 @@ __host__ __device__ __forceinline__ bool small_plan(const DecodeParams& a) {
 }
 
 
-// NT threads (256 or 1024: at least kTailClasses).
+// Maximum over each run of NW lanes of a wave (the value repeats every NW lanes).
+template <int NW>
+__device__ __forceinline__ int lanes_max(int v) {
+  return lanes_reduce<NW>(v, MaxOp());
+}
+
+// Block-wide sums of four values at once (one pair of barriers).
 template <int NT>
+__device__ __forceinline__ int4 block_sum4(int4 v, int4* scratch) {
+  constexpr int NW = NT / 64;
+  v = make_int4(wave_sum(v.x), wave_sum(v.y), wave_sum(v.z), wave_sum(v.w));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int4 u = scratch[threadIdx.x & (NW - 1)];
+  return make_int4(lanes_sum<NW>(u.x), lanes_sum<NW>(u.y), lanes_sum<NW>(u.z), lanes_sum<NW>(u.w));
+}
+
+// NT threads (256 or 1024: at least kTailClasses).  GROUPS: the batch may
+// come with shared-prefix groups (only then is LDS kept for them).
+template <int NT, bool GROUPS>
 __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size) {
   static_assert(NT >= kTailClasses && NT % 64 == 0 && NT <= 1024, "planner width");
   constexpr int NW = NT / 64;
+  // Sequences one thread handles in the group stage: all S <= kLensCached of
+  // a batch with groups for 1024 threads; 256 threads plan batches of at
+  // most 256 sequences.
+  constexpr int kPer = NT == 1024 ? kLensCached / NT : 1;
   __shared__ int lens_c[kLensCached];
-  __shared__ int start_c[kLensCached];   // shared-prefix blocks per sequence
   __shared__ int cls_off[kTailClasses];
   __shared__ int wave_sum[16];
   __shared__ int chunk_incl[NT];
@@ -306,7 +385,8 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   __shared__ int pitems_end;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.num_seqs;
-  bool prefix = a.num_groups > 0;   // then S <= kLensCached (checked on the host)
+  // With groups, S <= kLensCached (checked on the host).
+  const bool groups = GROUPS && a.num_groups > 0 && S <= NT * kPer;
 
   for (int i = tid; i < kTailClasses; i += NT) cls_off[i] = 0;
   if (tid == 0) {
@@ -320,63 +400,140 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // Group g's bounds and prefix hint, read by thread g (for the first NT
   // groups) together with the lengths, in one memory round trip.
   int reg_lo = 0, reg_hi = 0, reg_pb = 0;
-  if (prefix && tid < a.num_groups) {
+  if (groups && tid < a.num_groups) {
     reg_lo = a.group_starts[tid];
     reg_hi = a.group_starts[tid + 1];
     reg_pb = a.prefix_blocks[tid];
   }
-  // Groups must be ordered (group_starts non-decreasing), so that no two
-  // overlap: a sequence then belongs to one group at most and the prefix work
-  // list fits its S * num_parts_max entries.  Otherwise the groups are
-  // ignored and the batch is decoded plainly (the same result).
-  if (prefix) {
-    int bad = 0;
-    for (int g = tid; g < a.num_groups; g += NT) {
-      const int lo = g < NT ? reg_lo : a.group_starts[g];
-      const int hi = g < NT ? reg_hi : a.group_starts[g + 1];
-      bad |= hi < lo;
-    }
-    prefix = block_sum<NT>(bad, wave_sum) == 0;
-  }
   // One pass over the context lengths (clamped), kept in LDS for the passes
   // below.  S * max_blocks fits in int32 (checked on the host).
-  for (int s = tid; s < S; s += NT) {
+  for (int s = tid; s < S; s += NT)
     if (s < kLensCached) lens_c[s] = clamp_len(a, s, block_size);
-    if (prefix) start_c[s] = 0;
-  }
-  __syncthreads();
   auto len_of = [&](int s) { return s < kLensCached ? lens_c[s] : clamp_len(a, s, block_size); };
-  auto start_of = [&](int s) { return prefix ? start_c[s] : 0; };
 
-  // Shared prefixes.  A group's prefix is the run of whole blocks that its
-  // table entries share and that lies inside every member's context; it is
-  // read once per `per_item` sequences.  A group of one shares nothing.
-  const int per_item = prefix ? (a.prefix_rows / a.group > 0 ? a.prefix_rows / a.group : 1) : 1;
-  auto group_range = [&](int g, int& lo, int& hi) {
-    lo = max(g == tid ? reg_lo : a.group_starts[g], 0);
-    hi = min(g == tid ? reg_hi : a.group_starts[g + 1], S);
+  // Shared prefixes, one thread per sequence.  A group's prefix is the run of
+  // whole blocks that its table entries share and that lies inside every
+  // member's context; it is read once per `per_item` sequences.  A group of
+  // one shares nothing.  Groups are consecutive runs of sequences, so a
+  // sequence's group is the one whose first member is the nearest group
+  // start at or before it (a running maximum over the sequences), unless a
+  // group-less stretch starts in between.  The groups must be ordered
+  // (group_starts non-decreasing), so that no two overlap: a sequence then
+  // belongs to one group at most and the prefix work list fits its
+  // S * num_parts_max entries.  Otherwise the groups are ignored and the
+  // batch is decoded plainly (the same result).
+  int* start_c = nullptr;     // per sequence: its shared blocks
+  int16_t* bound_c = nullptr; // per sequence: 2 * s + 1 if a group of two or more starts
+                              //  at s, 2 * s if a group of one or a group-less run does,
+                              //  else -1; later, at a group's start: its end
+  int* gmin_c = nullptr;      // at a group's start: min(hint * block_size, member contexts)
+  if constexpr (GROUPS) {
+    __shared__ int start_s[kLensCached];
+    __shared__ int16_t bound_s[kLensCached];
+    start_c = start_s;
+    bound_c = bound_s;
+    gmin_c = start_s;         // start_c is written only after the minima are read
+  }
+  const int per_item = groups ? (a.prefix_rows / a.group > 0 ? a.prefix_rows / a.group : 1) : 1;
+  auto group_at = [&](int g, int& lo_raw, int& hi_raw, int& hint) {
+    lo_raw = g < NT ? reg_lo : a.group_starts[g];
+    hi_raw = g < NT ? reg_hi : a.group_starts[g + 1];
+    hint = g < NT ? reg_pb : a.prefix_blocks[g];
   };
-  int pre_mine = 0;
-  const int num_groups = prefix ? a.num_groups : 0;
-  if (prefix) {
-    for (int g = tid; g < num_groups; g += NT) {
-      int lo, hi;
-      group_range(g, lo, hi);
-      if (hi - lo < 2) continue;
-      int minL = len_of(lo);
-      for (int s = lo + 1; s < hi; ++s) minL = min(minL, len_of(s));
-      const int P = min(g == tid ? reg_pb : a.prefix_blocks[g], minL / block_size);
-      if (P <= 0) continue;
-      for (int s = lo; s < hi; ++s) start_c[s] = P;
-      pre_mine += (hi - lo + per_item - 1) / per_item * P;
+  // Own sequences of the group stage: the contiguous run s0 .. s0 + per - 1.
+  const int per = (S + NT - 1) / NT;
+  const int s0 = tid * per;
+  int head[kPer], pshared[kPer];   // own sequence s0 + j: group start (-1: none), shared blocks
+  int bad = 0, pre_mine = 0, mine_pre = 0, mine = 0;
+  if (groups) {
+    for (int s = tid; s < S; s += NT) bound_c[s] = -1;
+    __syncthreads();
+    for (int g = tid; g < a.num_groups; g += NT) {
+      int lo_raw, hi_raw, hint;
+      group_at(g, lo_raw, hi_raw, hint);
+      bad |= hi_raw < lo_raw;
+      const int lo = max(lo_raw, 0), hi = min(hi_raw, S);
+      if (lo < hi) {
+        bound_c[lo] = (int16_t)(2 * lo + (hi - lo >= 2));
+        if (hi - lo >= 2) gmin_c[lo] = min(max(hint, 0), a.max_blocks) * block_size;
+      }
+      if (g == a.num_groups - 1 && hi >= 0 && hi < S) bound_c[hi] = (int16_t)(2 * hi);
+    }
+    __syncthreads();
+    // The nearest marker at or before each sequence: a running maximum over
+    // the thread's own run, then over the runs of the threads before it.
+    int key[kPer];
+    int run = -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (j < per && s0 + j < S) run = max(run, (int)bound_c[s0 + j]);
+      key[j] = run;
+    }
+    const int incl = wave_scan_max(run);
+    __shared__ int wave_max[16];
+    if (lane == 63) wave_max[wave] = incl;
+    const int up = dpp_read<kDppWaveShr1>(-1, incl);   // lanes before this one
+    __syncthreads();
+    const int wm = wave_max[lane & (NW - 1)];
+    const int before = max(up, lanes_max<NW>((lane & (NW - 1)) < wave ? wm : -1));
+    // Shortest context of each group.  The thread folds each run of one
+    // group among its sequences and sends all but its last run to LDS; the
+    // last runs are folded across the wave first (lanes whose last run is
+    // one group's are adjacent: group starts do not decrease along the
+    // sequences) and sent by the segment's last lane, so a group of 1024
+    // sequences takes 16 LDS atomics on one address, not 1024.
+    int cur = -1, cmin = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int s = s0 + j;
+      const int k = max(key[j], before);
+      const bool mine_s = j < per && s < S;
+      head[j] = mine_s && k >= 0 && (k & 1) ? k >> 1 : -1;
+      pshared[j] = 0;
+      if (mine_s && head[j] != cur) {
+        if (cur >= 0) atomicMin(&gmin_c[cur], cmin);
+        cur = head[j];
+        cmin = INT_MAX;
+      }
+      if (head[j] >= 0) cmin = min(cmin, len_of(s));
+    }
+    cmin = segment_min(cmin, cur);
+    const int next = dpp_read<kDppWaveShl1>(-2, cur);
+    if (cur >= 0 && next != cur) atomicMin(&gmin_c[cur], cmin);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int s = s0 + j;
+      if (j >= per || s >= S) continue;
+      const int nblk = (len_of(s) + block_size - 1) / block_size;
+      pshared[j] = head[j] >= 0 ? gmin_c[head[j]] / block_size : 0;
+      mine_pre += nblk - pshared[j];
+      if (pshared[j] > 0 && (s - head[j]) % per_item == 0) pre_mine += pshared[j];
+    }
+    // Each group's end at its start, for the prefix work list (the markers
+    // are no longer read).
+    for (int g = tid; g < a.num_groups; g += NT) {
+      int lo_raw, hi_raw, hint;
+      group_at(g, lo_raw, hi_raw, hint);
+      const int lo = max(lo_raw, 0), hi = min(hi_raw, S);
+      if (hi - lo >= 2) bound_c[lo] = (int16_t)hi;
     }
   }
-  // (The sum's barriers also publish start_c.)
-  const int64_t pre_total = prefix ? block_sum<NT>(pre_mine, wave_sum) : 0;
-  int mine = 0;
-  for (int s = tid; s < S; s += NT)
-    mine += (len_of(s) + block_size - 1) / block_size - start_of(s);
-  const int64_t total = block_sum<NT>(mine, wave_sum);
+  for (int s = tid; s < S; s += NT) mine += (len_of(s) + block_size - 1) / block_size;
+  __shared__ int4 sum4[16];
+  const int4 sums = block_sum4<NT>(make_int4(bad, pre_mine, mine_pre, mine), sum4);
+  const bool prefix = groups && sums.x == 0;
+  const int64_t pre_total = prefix ? sums.y : 0;
+  const int64_t total = prefix ? sums.z : sums.w;
+  if (groups) {
+    // After the sums' barriers: every minimum has been read.
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (j < per && s0 + j < S) start_c[s0 + j] = prefix ? pshared[j] : 0;
+    __syncthreads();
+  }
+  // Shared blocks of sequence s.
+  auto start_of = [&](int s) { return prefix ? start_c[s] : 0; };
 
   // Partition size (choose_part_blocks).  Long partitions mean few partition
   // states to merge; short ones spread a long context over many workgroups.
@@ -426,12 +583,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
         a.ws_split[at] = make_int2(s, npre + nown);
       }
     }
-    int incl = nfull;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
+    const int incl = wave_scan_sum(nfull);
     if (lane == 63) wave_sum[wave] = incl;
     if (nfull > kDirectItems) long_seen = 1;
     __syncthreads();
@@ -471,12 +623,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   // class counts by the first kTailClasses threads (4 waves).
   {
     const int n = tid < kTailClasses ? cls_off[tid] : 0;
-    int incl = n;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
+    const int incl = wave_scan_sum(n);
     if (lane == 63 && wave < kTailClasses / 64) wave_sum[wave] = incl;
     __syncthreads();
     if (tid < kTailClasses) {
@@ -504,28 +651,26 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 
   // Prefix work list: (first sequence, sequences, partition, prefix blocks)
   // for every run of per_item sequences of a group and every partition of
-  // its prefix.  The order is arbitrary (it never changes the result).
-  // With ordered groups the list holds at most sum over groups of members *
-  // ceil(P / pbp) <= S * num_parts_max entries; the bound is checked anyway,
-  // so that no input can make the planner write past the list.
+  // its prefix, listed by the thread of the run's first sequence.  The order
+  // is arbitrary (it never changes the result).  With ordered groups the
+  // list holds at most sum over groups of members * ceil(P / pbp) <=
+  // S * num_parts_max entries; the bound is checked anyway, so that no input
+  // can make the planner write past the list.
   if (prefix) {
     const int64_t cap = (int64_t)S * a.num_parts_max;
-    for (int g = tid; g < num_groups; g += NT) {
-      int lo, hi;
-      group_range(g, lo, hi);
-      if (hi - lo < 2) continue;
-      const int P = start_c[lo];
-      if (P <= 0) continue;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int s = s0 + j;
+      if (j >= per || s >= S || pshared[j] <= 0 || (s - head[j]) % per_item != 0) continue;
+      const int P = pshared[j];
+      const int n = min(per_item, (int)bound_c[head[j]] - s);
       const int np = (P + pbp - 1) / pbp;
-      for (int f = lo; f < hi; f += per_item) {
-        const int n = min(per_item, hi - f);
-        const int at = atomicAdd(&npitems, np);
-        if ((int64_t)at + np > cap) {
-          atomicMin(&pitems_end, at);
-          continue;
-        }
-        for (int p = 0; p < np; ++p) a.ws_pitems[at + p] = make_int4(f, n, p, P);
+      const int at = atomicAdd(&npitems, np);
+      if ((int64_t)at + np > cap) {
+        atomicMin(&pitems_end, at);
+        continue;
       }
+      for (int p = 0; p < np; ++p) a.ws_pitems[at + p] = make_int4(s, n, p, P);
     }
     __syncthreads();
     if (tid == 0) a.ws_ctrl[kCtrlPrefixItems] = min(npitems, pitems_end);
@@ -540,12 +685,12 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
 // it are shifts.
 // NT threads: one wave for batches plan_small plans, 256 for up to 256
 // sequences, else 1024 (chosen by launch_decode_shape).
-template <int BS, int NT>
+template <int BS, int NT, bool GROUPS>
 __global__ __launch_bounds__(NT) void plan_items(DecodeParams a) {
   if constexpr (NT == 64) {
     plan_small<BS>(a);
   } else {
-    plan_body<NT>(a, BS);
+    plan_body<NT, GROUPS>(a, BS);
   }
 }
 
@@ -556,7 +701,7 @@ __global__ __launch_bounds__(1024) void write_and_plan(DecodeParams a, WriteArgs
       if (threadIdx.x < 64) plan_small<BS>(a);
       return;
     }
-    plan_body<1024>(a, BS);
+    plan_body<1024, false>(a, BS);   // a step has no shared-prefix groups
     return;
   }
   write_elements<E>(w, (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x,
@@ -1862,11 +2007,15 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
       hipLaunchKernelGGL((write_and_plan<uint32_t, BS>), grid, dim3(1024), 0, stream, p, *write);
   } else {
     if (small_plan(p))
-      hipLaunchKernelGGL((plan_items<BS, 64>), dim3(1), dim3(64), 0, stream, p);
+      hipLaunchKernelGGL((plan_items<BS, 64, false>), dim3(1), dim3(64), 0, stream, p);
+    else if (p.num_seqs <= 256 && prefix)
+      hipLaunchKernelGGL((plan_items<BS, 256, true>), dim3(1), dim3(256), 0, stream, p);
     else if (p.num_seqs <= 256)
-      hipLaunchKernelGGL((plan_items<BS, 256>), dim3(1), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((plan_items<BS, 256, false>), dim3(1), dim3(256), 0, stream, p);
+    else if (prefix)
+      hipLaunchKernelGGL((plan_items<BS, 1024, true>), dim3(1), dim3(1024), 0, stream, p);
     else
-      hipLaunchKernelGGL((plan_items<BS, 1024>), dim3(1), dim3(1024), 0, stream, p);
+      hipLaunchKernelGGL((plan_items<BS, 1024, false>), dim3(1), dim3(1024), 0, stream, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -227,3 +227,56 @@ def test_random_groupings(seed):
     _say(f"  max-abs err {err:.2e}")
     assert np.isfinite(out).all()
     _bars(err)
+
+
+def _grouped_batch(rng, head, sizes, tail, prefix, bs, Hq, Hkv, D):
+    """`head` group-less sequences, then groups of the given sizes (0: an
+    empty group), then `tail` group-less sequences after the last group."""
+    lens, groups, starts, hints = [], [], [head], []
+    lens += [int(x) for x in rng.integers(1, 200, head)]
+    for n in sizes:
+        first = len(lens)
+        lens += [prefix * bs + int(x) for x in rng.integers(1, 120, n)]
+        if n:
+            groups.append(list(range(first, first + n)))
+        starts.append(len(lens))
+        # hints: the shared count, one less, or none (a hint above the shared
+        # count is clamped only by the members' lengths, not by their tables)
+        hints.append(int(rng.choice([prefix, prefix, max(prefix - 1, 0), 0])))
+    lens += [int(x) for x in rng.integers(1, 200, tail)]
+    w = _custom(lens, groups, prefix, Hq, Hkv, D, bs, seed=int(rng.integers(1 << 30)))
+    return w, starts, hints
+
+
+@pytest.mark.parametrize("S_target", [300, 1500, 4100])
+def test_many_sequences_and_large_groups(S_target):
+    """Batches past 256 sequences (the 1024-thread planner; at 1500 and 4100
+    its per-sequence group search runs over two and five chunks of 1024):
+    group-less sequences first and last, one group of 40% of the batch,
+    groups of 1..40 with empty groups among them; against the oracle, and
+    bitwise reproducible."""
+    rng = np.random.default_rng(S_target)
+    big = int(0.4 * S_target)
+    sizes = [big]
+    while 10 + sum(sizes) < S_target - 60:
+        sizes.append(0 if rng.random() < 0.1 else int(rng.integers(1, 41)))
+    w, starts, hints = _grouped_batch(rng, 10, sizes, 50, 3, 16, 8, 2, 64)
+    _say(f"S={w.num_seqs} groups={len(sizes)} largest={big}")
+    out, _ = _prefix_run(w, starts, hints)
+    ref = _oracle(w)
+    err = float(np.abs(out - ref).max())
+    _say(f"  max-abs err {err:.2e}")
+    _bars(err)
+
+
+def test_groups_clamped_to_the_batch():
+    """group_starts below 0 and past num_seqs are clamped; a last group that
+    is empty ends the grouped run early."""
+    w = _custom([100, 120, 140, 90, 95, 99, 130], [[0, 1, 2], [4, 5, 6]], 4, 16, 4, 128, 16,
+                seed=11)
+    ref = _oracle(w)
+    for starts, pbl in (([-5, 3, 4, 99], [4, 4, 4]),      # [0,3) [3,4) [4,7)
+                        ([-9, -2, 3, 3], [4, 4, 4]),      # empty, [0,3), empty
+                        ([0, 3, 3, 4, 7, 7], [4, 0, 4, 4, 4])):
+        out, _ = _prefix_run(w, starts, pbl)
+        _bars(float(np.abs(out - ref).max()))
