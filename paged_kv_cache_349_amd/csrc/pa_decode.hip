@@ -208,6 +208,27 @@ struct MaxOp {
 __device__ __forceinline__ int wave_scan_sum(int v) { return wave_scan(v, 0, AddOp()); }
 __device__ __forceinline__ int wave_scan_max(int v) { return wave_scan(v, INT_MIN, MaxOp()); }
 
+// Float sum and maximum over a wave, every lane gets the result (the order
+// of the additions is fixed, so the result is reproducible).
+struct AddFOp {
+  __device__ int operator()(int a, int b) const {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }
+};
+struct MaxFOp {
+  __device__ int operator()(int a, int b) const {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }
+};
+__device__ __forceinline__ float wave_sum_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_readlane(wave_scan(__float_as_int(v), 0, AddFOp()), 63));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(
+      wave_scan(__float_as_int(v), __float_as_int(-__builtin_inff()), MaxFOp()), 63));
+}
+
 // Sum over a wave (every lane gets it).
 __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane(wave_scan_sum(v), 63);
@@ -297,28 +318,38 @@ __device__ __forceinline__ void plan_small(const DecodeParams& a) {
   const int n_full = __builtin_amdgcn_readlane(incl, 63);
   for (int p = 0; p < min(nfull, kDirectItems); ++p)
     a.ws_items[base + p] = make_int4(lane, p, L, 0);
-  if (__builtin_amdgcn_ballot_w64(nfull > kDirectItems)) {
-    for (int j = 0; j < S; ++j) {
-      const int nj = __builtin_amdgcn_readlane(nfull, j);
-      if (nj <= kDirectItems) continue;
-      const int bj = __builtin_amdgcn_readlane(base, j);
-      const int Lj = __builtin_amdgcn_readlane(L, j);
-      for (int p = kDirectItems + lane; p < nj; p += 64) a.ws_items[bj + p] = make_int4(j, p, Lj, 0);
-    }
+  for (uint64_t longs = __builtin_amdgcn_ballot_w64(nfull > kDirectItems); longs;
+       longs &= longs - 1) {
+    const int j = __builtin_ctzll(longs);
+    const int nj = __builtin_amdgcn_readlane(nfull, j);
+    const int bj = __builtin_amdgcn_readlane(base, j);
+    const int Lj = __builtin_amdgcn_readlane(L, j);
+    for (int p = kDirectItems + lane; p < nj; p += 64) a.ws_items[bj + p] = make_int4(j, p, Lj, 0);
   }
-  // Partial last partitions after all full ones, by decreasing size.
+  // Partial last partitions after all full ones, by decreasing size (ties by
+  // sequence).  A lane's rank: the lanes with a larger remainder, found bit
+  // by bit from the top (`same`: the lanes whose remainder has agreed with
+  // this lane's so far; at a bit where this lane has 0, those with 1 are
+  // larger), then the earlier lanes with the same remainder.
   const int rem = nblk % pb;
   const bool tail = live && rem != 0;
+  const uint64_t below = (1ull << lane) - 1;
+  uint64_t same = __builtin_amdgcn_ballot_w64(tail);
   int rank = 0;
-  for (int j = 0; j < S; ++j) {
-    const int rj = __builtin_amdgcn_readlane(rem, j);
-    rank += rj != 0 && (rj > rem || (rj == rem && j < lane));
+  for (int b = 31 - __builtin_clz(pb); b >= 0; --b) {   // rem < pb
+    const uint64_t ones = __builtin_amdgcn_ballot_w64((rem >> b) & 1);
+    if ((rem >> b) & 1) {
+      same &= ones;
+    } else {
+      rank += __builtin_popcountll(same & ones);
+      same &= ~ones;
+    }
   }
+  rank += __builtin_popcountll(same & below);
   if (tail) a.ws_items[n_full + rank] = make_int4(lane, nblk / pb, L, 0);
   // Sequences whose partition states are merged: up to kMergeShort
   // partitions from the front of the split list, longer ones from the back.
   const int nparts = (nblk + pb - 1) / pb;
-  const uint64_t below = (1ull << lane) - 1;
   const uint64_t short_split = __builtin_amdgcn_ballot_w64(live && nparts > 1 && nparts <= kMergeShort);
   const uint64_t long_split = __builtin_amdgcn_ballot_w64(live && nparts > kMergeShort);
   if (live && nparts > 1) {
@@ -1840,8 +1871,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     }
     float m = kNegInf;
     for (int p = tid; p < nparts; p += kMergeThreads) m = fmaxf(m, ml[(prow + p) * G + gq].x);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, shfl_xor_f(m, off));
+    m = wave_max_f(m);
     if (lane == 0) head_max[wave] = m;
     __syncthreads();
     float M = kNegInf;
@@ -1854,8 +1884,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
         if (v.x != kNegInf) l += v.y * exp2_fast(v.x - M);
       }
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) l += shfl_xor_f(l, off);
+    l = wave_sum_f(l);
     if (lane == 0) head_sum[wave] = l;
     f4 val = {0.f, 0.f, 0.f, 0.f};
     if (M != kNegInf) {
