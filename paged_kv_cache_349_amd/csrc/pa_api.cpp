@@ -241,6 +241,7 @@ static int decode_common(float* out, const void* q, const void* k_cache, const v
   p.prefix_rows = 0;   // set by the launcher
   p.ws_pitems = prefix ? (int4*)(ws + lay.pitems_off) : nullptr;
   p.packed_pool = (flags & PA_FLAG_PACKED_POOL) ? 1 : 0;
+  p.inline_plan = 0;   // set by the launcher
   const auto ev = next_timing_events();
   hipError_t e = pa::launch_decode(p, sizeof(pa::DecodeParams), (pa::KvType)kv_dtype, head_dim,
                                    block_size, (flags & PA_FLAG_VECTOR_ALU) != 0,

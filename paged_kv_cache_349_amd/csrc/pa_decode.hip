@@ -294,77 +294,103 @@ __device__ __forceinline__ int choose_part_blocks(const DecodeParams& a, int64_t
   return pb;
 }
 
-// The planner of a batch of at most 64 sequences without shared prefixes, in
-// one wave with no barrier: lane s plans sequence s.  Its lists are those of
-// plan_body (same partition size, same items, same split sequences) except
-// for the order of the partial last partitions -- here by decreasing size,
-// ties by sequence -- and of the split list, neither of which changes a
-// result.
+// The plan of a batch of at most 64 sequences without shared prefixes, in
+// one wave's registers: lane s holds sequence s.  The work list is the full
+// partitions in sequence order (an empty sequence gets one item that zeroes
+// its output), then the partial last partitions by decreasing size, ties by
+// sequence.  It is plan_body's list (same partition size, same items, same
+// split sequences) except for the order of the partial partitions and of
+// the split list, neither of which changes a result.
+struct LanePlan {
+  int L, nblk;       // this lane's sequence: context (clamped), blocks
+  int nfull, incl;   // its full partitions; those of sequences 0 .. s
+  int rank;          // position of its partial partition among them
+  bool tail;         // it has a partial last partition
+  int pb;            // partition size in blocks (uniform)
+  int n_full, n_tail;
+};
+
 template <int BS>
-__device__ __forceinline__ void plan_small(const DecodeParams& a) {
+__device__ __forceinline__ LanePlan lane_plan(const DecodeParams& a) {
+  LanePlan q;
   const int lane = threadIdx.x & 63;
-  const int S = a.num_seqs;
-  const bool live = lane < S;
-  const int L = live ? clamp_len(a, lane, BS) : 0;
-  const int nblk = (L + BS - 1) / BS;
-  const int pb = choose_part_blocks(a, wave_sum(nblk), a.decode_grid, a.balance);
-  const int pbp = choose_part_blocks(a, 0, a.decode_grid / 2, 0);
-  // Full partitions in sequence order (an empty sequence gets one item that
-  // zeroes its output); a sequence's first kDirectItems are listed by its
-  // lane, any further ones by all lanes together.
-  const int nfull = live ? (nblk == 0 ? 1 : nblk / pb) : 0;
-  const int incl = wave_scan_sum(nfull);
-  const int base = incl - nfull;
-  const int n_full = __builtin_amdgcn_readlane(incl, 63);
-  for (int p = 0; p < min(nfull, kDirectItems); ++p)
-    a.ws_items[base + p] = make_int4(lane, p, L, 0);
-  for (uint64_t longs = __builtin_amdgcn_ballot_w64(nfull > kDirectItems); longs;
-       longs &= longs - 1) {
-    const int j = __builtin_ctzll(longs);
-    const int nj = __builtin_amdgcn_readlane(nfull, j);
-    const int bj = __builtin_amdgcn_readlane(base, j);
-    const int Lj = __builtin_amdgcn_readlane(L, j);
-    for (int p = kDirectItems + lane; p < nj; p += 64) a.ws_items[bj + p] = make_int4(j, p, Lj, 0);
-  }
-  // Partial last partitions after all full ones, by decreasing size (ties by
-  // sequence).  A lane's rank: the lanes with a larger remainder, found bit
-  // by bit from the top (`same`: the lanes whose remainder has agreed with
-  // this lane's so far; at a bit where this lane has 0, those with 1 are
-  // larger), then the earlier lanes with the same remainder.
-  const int rem = nblk % pb;
-  const bool tail = live && rem != 0;
-  const uint64_t below = (1ull << lane) - 1;
-  uint64_t same = __builtin_amdgcn_ballot_w64(tail);
-  int rank = 0;
-  for (int b = 31 - __builtin_clz(pb); b >= 0; --b) {   // rem < pb
+  const bool live = lane < a.num_seqs;
+  q.L = live ? clamp_len(a, lane, BS) : 0;
+  q.nblk = (q.L + BS - 1) / BS;
+  q.pb = choose_part_blocks(a, wave_sum(q.nblk), a.decode_grid, a.balance);
+  q.nfull = live ? (q.nblk == 0 ? 1 : q.nblk / q.pb) : 0;
+  q.incl = wave_scan_sum(q.nfull);
+  q.n_full = __builtin_amdgcn_readlane(q.incl, 63);
+  // A lane's rank: the lanes with a larger remainder, found bit by bit from
+  // the top (`same`: the lanes whose remainder has agreed with this lane's so
+  // far; at a bit where this lane has 0, those with 1 are larger), then the
+  // earlier lanes with the same remainder.
+  const int rem = q.nblk % q.pb;
+  q.tail = live && rem != 0;
+  uint64_t same = __builtin_amdgcn_ballot_w64(q.tail);
+  q.n_tail = __builtin_popcountll(same);
+  q.rank = 0;
+  for (int b = 31 - __builtin_clz(q.pb); b >= 0; --b) {   // rem < pb
     const uint64_t ones = __builtin_amdgcn_ballot_w64((rem >> b) & 1);
     if ((rem >> b) & 1) {
       same &= ones;
     } else {
-      rank += __builtin_popcountll(same & ones);
+      q.rank += __builtin_popcountll(same & ones);
       same &= ~ones;
     }
   }
-  rank += __builtin_popcountll(same & below);
-  if (tail) a.ws_items[n_full + rank] = make_int4(lane, nblk / pb, L, 0);
-  // Sequences whose partition states are merged: up to kMergeShort
-  // partitions from the front of the split list, longer ones from the back.
-  const int nparts = (nblk + pb - 1) / pb;
+  q.rank += __builtin_popcountll(same & ((1ull << lane) - 1));
+  return q;
+}
+
+// The split list of a lane plan and its counts (what merge_splits reads):
+// sequences spanning several partitions, up to kMergeShort partitions from
+// the front of the list, longer ones from the back.
+__device__ __forceinline__ void write_split_list(const DecodeParams& a, const LanePlan& q) {
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < a.num_seqs;
+  const int nparts = (q.nblk + q.pb - 1) / q.pb;
+  const uint64_t below = (1ull << lane) - 1;
   const uint64_t short_split = __builtin_amdgcn_ballot_w64(live && nparts > 1 && nparts <= kMergeShort);
   const uint64_t long_split = __builtin_amdgcn_ballot_w64(live && nparts > kMergeShort);
   if (live && nparts > 1) {
     const int at = nparts <= kMergeShort ? __builtin_popcountll(short_split & below)
-                                         : S - 1 - __builtin_popcountll(long_split & below);
+                                         : a.num_seqs - 1 - __builtin_popcountll(long_split & below);
     a.ws_split[at] = make_int2(lane, nparts);
   }
-  const int n_tail = __builtin_popcountll(__builtin_amdgcn_ballot_w64(tail));
   if (lane == 0) {
-    a.ws_ctrl[kCtrlEntries] = n_full + n_tail;
-    a.ws_ctrl[kCtrlPartBlocks] = pb;
     a.ws_ctrl[kCtrlSplits] = __builtin_popcountll(short_split);
+    a.ws_ctrl[kCtrlLongSplits] = __builtin_popcountll(long_split);
+  }
+}
+
+// The planner of such a batch, in one wave with no barrier: the lane plan
+// written out as the work list.
+template <int BS>
+__device__ __forceinline__ void plan_small(const DecodeParams& a) {
+  const int lane = threadIdx.x & 63;
+  const LanePlan q = lane_plan<BS>(a);
+  const int pbp = choose_part_blocks(a, 0, a.decode_grid / 2, 0);
+  // A sequence's first kDirectItems full partitions are listed by its lane,
+  // any further ones by all lanes together.
+  const int base = q.incl - q.nfull;
+  for (int p = 0; p < min(q.nfull, kDirectItems); ++p)
+    a.ws_items[base + p] = make_int4(lane, p, q.L, 0);
+  for (uint64_t longs = __builtin_amdgcn_ballot_w64(q.nfull > kDirectItems); longs;
+       longs &= longs - 1) {
+    const int j = __builtin_ctzll(longs);
+    const int nj = __builtin_amdgcn_readlane(q.nfull, j);
+    const int bj = __builtin_amdgcn_readlane(base, j);
+    const int Lj = __builtin_amdgcn_readlane(q.L, j);
+    for (int p = kDirectItems + lane; p < nj; p += 64) a.ws_items[bj + p] = make_int4(j, p, Lj, 0);
+  }
+  if (q.tail) a.ws_items[q.n_full + q.rank] = make_int4(lane, q.nblk / q.pb, q.L, 0);
+  write_split_list(a, q);
+  if (lane == 0) {
+    a.ws_ctrl[kCtrlEntries] = q.n_full + q.n_tail;
+    a.ws_ctrl[kCtrlPartBlocks] = q.pb;
     a.ws_ctrl[kCtrlPrefixItems] = 0;
     a.ws_ctrl[kCtrlPrefixPart] = pbp;
-    a.ws_ctrl[kCtrlLongSplits] = __builtin_popcountll(long_split);
     a.ws_ctrl[kCtrlAbort] = 0;
   }
   if (lane < kClaimPools) a.ws_ctrl[kCtrlClaims + lane * kClaimStride] = 0;
@@ -1176,7 +1202,14 @@ struct Desc {
 // table entry per item instead of one per block, so comparing it with the
 // ordinary kernel on the same packed pool isolates the cost of the per-block
 // table reads from that of blocks scattered over the pool.
-template <int D, int BS, int W, bool PREFIX, bool TABLE = true>
+// PLAN = true (batches of at most 64 sequences without shared prefixes): no
+// planner launch before this one.  Every wave computes the batch's lane plan
+// (lane_plan) itself from the context lengths and finds an item's sequence
+// and partition in it; every round is dealt (no claim counters, so nothing in
+// the workspace has to be zeroed first); workgroup 0 writes the split list
+// for merge_splits.  A wait that gives up is recorded in its own word, which
+// merge_splits turns into the call's abort word.
+template <int D, int BS, int W, bool PREFIX, bool TABLE = true, bool PLAN = false>
 __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
@@ -1192,9 +1225,14 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   const PA_CONST int32_t* ctrl = as_const(a.ws_ctrl);
   const PA_CONST int32_t* items = as_const((const int32_t*)a.ws_items);   // int4 entries
   const PA_CONST int32_t* tables = as_const(a.tables);
-  const int total = ctrl[kCtrlEntries] * Hkv;
-  const int pb = ctrl[kCtrlPartBlocks];
-  const int pbp = ctrl[kCtrlPrefixPart];
+  LanePlan lp{};
+  if constexpr (PLAN) lp = lane_plan<BS>(a);
+  const int total = PLAN ? (lp.n_full + lp.n_tail) * Hkv : ctrl[kCtrlEntries] * Hkv;
+  const int pb = PLAN ? lp.pb : ctrl[kCtrlPartBlocks];
+  const int pbp = PLAN ? 1 : ctrl[kCtrlPrefixPart];
+  if constexpr (PLAN) {
+    if (bid == 0 && w == 0) write_split_list(a, lp);
+  }
   __shared__ int s_count[kMaxLdsSlots];   // waves that finished the slot's item
   __shared__ int s_epoch[kMaxLdsSlots];   // item the slot is free for
 
@@ -1202,8 +1240,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // a legitimate one lasts microseconds) means a broken invariant: record it
   // in the workspace and give up, so the kernel still ends.
   auto abort_wait = [&]() {
-    if (lane == 0) __hip_atomic_store(&a.ws_ctrl[kCtrlAbort], 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0)
+      __hip_atomic_store(&a.ws_ctrl[PLAN ? kCtrlAbortPlanned : kCtrlAbort],
+                         PLAN ? kAbortMark : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
 
   // The workgroup's item for round r.  The list (longest items first) is
@@ -1240,7 +1279,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // (round r gives item r*NG + b to workgroup b when r is even and to
   // workgroup NG-1-b when r is odd).
   auto item_of = [&](int r) -> int { return r * NG + ((r & 1) ? NG - 1 - bid : bid); };
-  const bool claimed_rounds = total >= 2 * NG;
+  const bool claimed_rounds = !PLAN && total >= 2 * NG;
   // Pools in use: kClaimPools, or fewer on a small grid, so that every pool
   // has a claimer (pool x holds workgroups 2x and 2x + 1 among others).
   const int npools = min(kClaimPools, max(1, NG >> kPoolShift));
@@ -1331,8 +1370,29 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     // one memory round trip: round 0's item is the workgroup's index, below
     // the list's capacity.  Fields of an item past the end are not used.
     const int e_idx = min(item / Hkv, a.num_seqs * a.num_parts_max - 1);
-    const int e_s = items[4 * e_idx + 0], e_part = items[4 * e_idx + 1];
-    const int e_L = items[4 * e_idx + 2], e_P = items[4 * e_idx + 3];
+    int e_s, e_part, e_L, e_P;
+    if constexpr (PLAN) {
+      // Entry e of the lane plan: full partition e - (first entry of s) of
+      // the sequence s whose full partitions cover e, or the partial
+      // partition of rank e - n_full.
+      if (e_idx < lp.n_full) {
+        e_s = __builtin_popcountll(
+            __builtin_amdgcn_ballot_w64(lane < a.num_seqs && lp.incl <= e_idx));
+        e_part = e_idx - (__builtin_amdgcn_readlane(lp.incl, e_s) -
+                          __builtin_amdgcn_readlane(lp.nfull, e_s));
+      } else {
+        const uint64_t at = __builtin_amdgcn_ballot_w64(lp.tail && lp.rank == e_idx - lp.n_full);
+        e_s = at ? __builtin_ctzll(at) : 0;
+        e_part = __builtin_amdgcn_readlane(lp.nblk, e_s) / pb;
+      }
+      e_L = __builtin_amdgcn_readlane(lp.L, e_s);
+      e_P = 0;
+    } else {
+      e_s = items[4 * e_idx + 0];
+      e_part = items[4 * e_idx + 1];
+      e_L = items[4 * e_idx + 2];
+      e_P = items[4 * e_idx + 3];
+    }
     d.s = d.valid ? e_s : 0;
     d.part = d.valid ? e_part : 0;
     d.L = d.valid ? e_L : 0;
@@ -1805,6 +1865,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   const int r = tid / C, c = tid - r * C;
   const int g = c / kCols4, d4 = c - g * kCols4;  // this thread's column
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  // After an attention kernel that planned the batch itself: the call's
+  // abort word from the one that kernel writes, which is cleared for the
+  // next such call (its waits record only the mark, never clear it).
+  if (a.inline_plan && blockIdx.x == 0 && tid == 0) {
+    a.ws_ctrl[kCtrlAbort] = a.ws_ctrl[kCtrlAbortPlanned] == kAbortMark;
+    a.ws_ctrl[kCtrlAbortPlanned] = 0;
+  }
   const int64_t n_short = (int64_t)a.ws_ctrl[kCtrlSplits] * Hkv;
   const int64_t n_long = (int64_t)a.ws_ctrl[kCtrlLongSplits] * Hkv;
 
@@ -1997,10 +2064,17 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   if (p.balance) p.balance = kWaves / 2;
   const bool prefix = p.num_groups > 0;   // bf16 matrix-core kernel only (checked by the API)
   const bool packed = p.packed_pool != 0;  // bf16 matrix-core kernel, no prefixes (checked by the API)
+  // A batch the one-wave planner would plan, decoded without a slot write in
+  // the same call, is planned inside the attention kernel instead: one
+  // launch less (merge_splits, which then always follows, reports its waits).
+  const bool plan_inside = type == KvType::BF16 && !vector_alu && !prefix && !packed && !write &&
+                           small_plan(p) && p.num_parts_max > 1;
+  p.inline_plan = plan_inside ? 1 : 0;
   if (type == KvType::BF16 && !vector_alu) {
     kernel = prefix ? (const void*)decode_mfma_bf16<D, BS, kWaves, true>
-                    : packed ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, false>
-                             : (const void*)decode_mfma_bf16<D, BS, kWaves, false>;
+             : packed ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, false>
+             : plan_inside ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, true, true>
+                           : (const void*)decode_mfma_bf16<D, BS, kWaves, false>;
     smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
     if (prefix) {
       const size_t pre = (size_t)prefix_lds_floats<D, kWaves>() * 4;
@@ -2034,7 +2108,7 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
       hipLaunchKernelGGL((write_and_plan<uint16_t, BS>), grid, dim3(1024), 0, stream, p, *write);
     else
       hipLaunchKernelGGL((write_and_plan<uint32_t, BS>), grid, dim3(1024), 0, stream, p, *write);
-  } else {
+  } else if (!plan_inside) {
     if (small_plan(p))
       hipLaunchKernelGGL((plan_items<BS, 64, false>), dim3(1), dim3(64), 0, stream, p);
     else if (p.num_seqs <= 256 && prefix)
@@ -2054,6 +2128,9 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
                        dim3(threads), smem, stream, p);
   else if (type == KvType::BF16 && !vector_alu && packed)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false, false>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else if (plan_inside)
+    hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false, true, true>), dim3(p.decode_grid),
                        dim3(threads), smem, stream, p);
   else if (type == KvType::BF16 && !vector_alu)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, false>), dim3(p.decode_grid),

@@ -50,6 +50,8 @@ struct DecodeParams {
   int4* ws_pitems;              // [S * num_parts_max] prefix work list:
                                 //  (first sequence, sequences, partition, prefix blocks)
   int32_t packed_pool;          // diagnostic: block j of sequence s is tables[s, 0] + j
+  int32_t inline_plan;          // the attention kernel plans the batch itself (no planner
+                                //  launch; set by the launcher)
 };
 
 // ws_ctrl slots written by the planner: work-list entries, chosen partition
@@ -64,8 +66,15 @@ constexpr int kCtrlLongSplits = 5;    // split sequences with more than kMergeSh
 constexpr int kMergeShort = 16;
 // Set by the decode kernel if one of its waits on other waves of its
 // workgroup did not end (a broken invariant; the output is then incomplete).
-// Cleared by the planner; read through pa_decode_check.
+// Cleared by the planner (or set by merge_splits, below); read through
+// pa_decode_check.
 constexpr int kCtrlAbort = 20;
+// The same for an attention kernel that plans the batch itself (no planner
+// launch clears anything before it): such a wait stores kAbortMark here, and
+// merge_splits, which always follows that kernel, sets kCtrlAbort to whether
+// the mark is present and clears this word.
+constexpr int kCtrlAbortPlanned = 21;
+constexpr int32_t kAbortMark = 0x5a17ab07;
 // Claim counters of the matrix-core kernel's work list, one per pool
 // (workgroups b with b % kClaimPools == x claim from pool x), each in a
 // 128-byte line of its own; zeroed by the planner.
