@@ -182,6 +182,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * num_heads / num_kv_heads in [1, 16], kv_dtype F32 or BF16.
  * The reduction order depends only on logical positions, so results are
  * bitwise reproducible and independent of where the blocks sit in the pool.
+ * The call's kernels: a planner (skipped for bf16 batches of at most 64
+ * sequences, which the attention kernel plans itself), the attention kernel,
+ * and a merge of split sequences (when a sequence can span two partitions).
  * The environment variable PA_NUM_CUS_OVERRIDE, if set, replaces the device's
  * CU count in how the kernel shares out its work, and PA_DECODE_GRID_OVERRIDE,
  * if set to a positive number below the default, the number of workgroups of
@@ -276,10 +279,13 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_hea
  * kernel's waves hand work to one another through the workgroup's shared
  * memory; each such wait is bounded, and a wait that does not end (a broken
  * invariant, never expected) is given up so that the kernel still ends:
- * that call's output is then incomplete.  The kernel records it in the int32
- * word at byte offset 80 of the workspace (the planner clears it at the start
- * of every call).  This call enqueues on `stream` a copy of that word into
- * *flag: 0 = every wait ended, 1 = the output of that call is incomplete.
+ * that call's output is then incomplete.  The call records it in the int32
+ * word at byte offset 80 of the workspace (set for every call: cleared by the
+ * planner launch at its start, or, for a batch of at most 64 sequences that
+ * the attention kernel plans itself, written by the call's last kernel from
+ * a word of that kernel's own).  This call enqueues on `stream` a copy of
+ * that word into *flag: 0 = every wait ended, 1 = the output of that call is
+ * incomplete.
  *   workspace   the workspace the decode call used (device, 256-byte aligned,
  *               workspace_bytes >= 4224, as any decode workspace is); NULL
  *               with workspace_bytes == 0 means pa_decode_noalloc's array
