@@ -105,6 +105,12 @@ struct WriteArgs {
   int32_t v_tile;       // tokens per feature-major V sub-tile: 16 if 16 | block_size, else block_size
   int64_t num_slots;    // num_blocks * block_size
   int32_t elem_bytes;   // 2 (bf16) or 4 (fp32)
+  // Shifts for head_dim, num_kv_heads, block_size and v_tile when all four
+  // are powers of two and element and slot indices fit in 31 bits (narrow);
+  // the index arithmetic then takes shifts and masks instead of 64-bit
+  // divisions.
+  int32_t narrow;
+  int32_t log2_d, log2_h, log2_bs, log2_vt;
 };
 
 WriteArgs make_write_args(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

@@ -43,6 +43,18 @@ WriteArgs make_write_args(void* k_cache, void* v_cache, const void* k_new, const
   w.v_tile = block_size % 16 == 0 ? 16 : block_size;
   w.num_slots = (int64_t)num_blocks * block_size;
   w.elem_bytes = type == KvType::BF16 ? 2 : 4;
+  auto log2_of = [](int64_t v) {   // -1 unless v is a power of two
+    if (v <= 0 || (v & (v - 1)) != 0) return -1;
+    int k = 0;
+    while ((int64_t(1) << k) < v) ++k;
+    return k;
+  };
+  w.log2_d = log2_of(head_dim);
+  w.log2_h = log2_of(num_kv_heads);
+  w.log2_bs = log2_of(block_size);
+  w.log2_vt = log2_of(w.v_tile);
+  w.narrow = w.log2_d >= 0 && w.log2_h >= 0 && w.log2_bs >= 0 && w.log2_vt >= 0 &&
+             w.total <= INT32_MAX && w.num_slots <= INT32_MAX;
   return w;
 }
 
