@@ -1872,13 +1872,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     a.ws_ctrl[kCtrlAbort] = a.ws_ctrl[kCtrlAbortPlanned] == kAbortMark;
     a.ws_ctrl[kCtrlAbortPlanned] = 0;
   }
-  const int64_t n_short = (int64_t)a.ws_ctrl[kCtrlSplits] * Hkv;
-  const int64_t n_long = (int64_t)a.ws_ctrl[kCtrlLongSplits] * Hkv;
+  // Unit counts fit in 31 bits (S * Hq is bounded on the host), so the unit
+  // arithmetic is 32-bit: a 64-bit division costs a wave hundreds of
+  // instructions before its first load.
+  const int n_short = a.ws_ctrl[kCtrlSplits] * Hkv;
+  const int n_long = a.ws_ctrl[kCtrlLongSplits] * Hkv;
 
   if (r < R) {
-    for (int64_t u = blockIdx.x + (int64_t)r * gridDim.x; u < n_short; u += (int64_t)gridDim.x * R) {
+    for (int u = blockIdx.x + r * gridDim.x; u < n_short; u += gridDim.x * R) {
       const int2 e = a.ws_split[u / Hkv];
-      const int h = (int)(u % Hkv);
+      const int h = u % Hkv;
       const int s = e.x, nparts = e.y;
       const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;   // partition 0's row
       float2 mlp[kMergeShort];
@@ -1917,11 +1920,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   // each, and the rows' partial sums are added in row order.
   constexpr int kRowsH = kMergeThreads / kCols4;
   const int rh = tid / kCols4, ch = tid - rh * kCols4;
-  for (int64_t u = gridDim.x - 1 - blockIdx.x; u < n_long * G; u += gridDim.x) {
-    const int64_t uh = u / G;                  // (split sequence, KV head)
+  for (int u = gridDim.x - 1 - blockIdx.x; u < n_long * G; u += gridDim.x) {
+    const int uh = u / G;                      // (split sequence, KV head)
     const int gq = (int)(u - uh * G);
     const int2 e = a.ws_split[S - 1 - uh / Hkv];
-    const int h = (int)(uh % Hkv);
+    const int h = uh % Hkv;
     const int s = e.x, nparts = e.y;
     const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
     const int p_lo = (int)((int64_t)nparts * rh / kRowsH);
