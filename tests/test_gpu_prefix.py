@@ -248,19 +248,22 @@ def _grouped_batch(rng, head, sizes, tail, prefix, bs, Hq, Hkv, D):
     return w, starts, hints
 
 
-@pytest.mark.parametrize("S_target", [300, 1500, 4100])
+@pytest.mark.parametrize("S_target", [300, 1500, 4100, 8192])
 def test_many_sequences_and_large_groups(S_target):
-    """Batches past 256 sequences (the 1024-thread planner; at 1500 and 4100
-    its per-sequence group search runs over two and five chunks of 1024):
+    """Batches past 256 sequences (the 1024-thread planner, whose threads own
+    1 to 8 consecutive sequences each in the group stage; 8192 is the most a
+    call with groups takes):
     group-less sequences first and last, one group of 40% of the batch,
     groups of 1..40 with empty groups among them; against the oracle, and
     bitwise reproducible."""
     rng = np.random.default_rng(S_target)
     big = int(0.4 * S_target)
     sizes = [big]
-    while 10 + sum(sizes) < S_target - 60:
+    while sum(sizes) + 40 < S_target - 60:      # 60 = 10 group-less first + 50 last
         sizes.append(0 if rng.random() < 0.1 else int(rng.integers(1, 41)))
+    sizes.append(S_target - 60 - sum(sizes))
     w, starts, hints = _grouped_batch(rng, 10, sizes, 50, 3, 16, 8, 2, 64)
+    assert w.num_seqs == S_target
     _say(f"S={w.num_seqs} groups={len(sizes)} largest={big}")
     out, _ = _prefix_run(w, starts, hints)
     ref = _oracle(w)
