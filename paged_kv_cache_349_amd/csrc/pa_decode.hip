@@ -12,7 +12,7 @@
 // logical positions, so results are bitwise reproducible and independent of
 // where blocks sit in the pool.
 //
-// Three launches on the caller's stream:
+// Up to three launches on the caller's stream:
 //   plan_items    one workgroup (sharing its launch with the slot write when
 //                 a whole step is issued).  Picks the partition size and
 //                 lists the non-empty (s, p) pairs in the workspace -- every
@@ -20,12 +20,16 @@
 //                 last partitions in decreasing size -- plus the sequences
 //                 whose partition states must be merged, and, with shared
 //                 prefixes, each group's shared blocks and the prefix items.
+//                 Not launched for a decode of at most 64 sequences without
+//                 shared prefixes: the matrix-core kernel then computes the
+//                 same plan itself (lane_plan).
 //   decode_*      persistent: as many workgroups as fit on the chip at once,
 //                 dealt the first round of the list and claiming the rest
-//                 from per-pool counters (the vector-ALU kernel deals every
-//                 round in snake order), so no workgroup is launched for an
-//                 empty partition and the workgroups end close together
-//                 however ragged the context lengths are.
+//                 from per-pool counters (the vector-ALU kernel and the
+//                 self-planning kernel deal every round in snake order), so
+//                 no workgroup is launched for an empty partition and the
+//                 workgroups end close together however ragged the context
+//                 lengths are.
 //   merge_splits  log-sum-exp merge of the partition states of every
 //                 sequence listed by the planner: per-head maxima and sums
 //                 first, then the weighted sum of the partitions' vectors.
@@ -432,7 +436,7 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   constexpr int kPer = NT == 1024 ? kLensCached / NT : 1;
   __shared__ int lens_c[kLensCached];
   __shared__ int cls_off[kTailClasses];
-  __shared__ int wave_sum[16];
+  __shared__ int wave_part[16];
   __shared__ int chunk_incl[NT];
   __shared__ int long_seen;
   __shared__ int run_base;
@@ -641,10 +645,10 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
       }
     }
     const int incl = wave_scan_sum(nfull);
-    if (lane == 63) wave_sum[wave] = incl;
+    if (lane == 63) wave_part[wave] = incl;
     if (nfull > kDirectItems) long_seen = 1;
     __syncthreads();
-    const int wsum = wave_sum[lane & (NW - 1)];
+    const int wsum = wave_part[lane & (NW - 1)];
     const int chunk = lanes_sum<NW>(wsum);
     const int before = lanes_sum<NW>((lane & (NW - 1)) < wave ? wsum : 0);
     // A sequence's first kDirectItems full partitions are listed by its own
@@ -681,11 +685,11 @@ __device__ __forceinline__ void plan_body(const DecodeParams& a, int block_size)
   {
     const int n = tid < kTailClasses ? cls_off[tid] : 0;
     const int incl = wave_scan_sum(n);
-    if (lane == 63 && wave < kTailClasses / 64) wave_sum[wave] = incl;
+    if (lane == 63 && wave < kTailClasses / 64) wave_part[wave] = incl;
     __syncthreads();
     if (tid < kTailClasses) {
       int before = run_base;
-      for (int w = 0; w < wave; ++w) before += wave_sum[w];
+      for (int w = 0; w < wave; ++w) before += wave_part[w];
       cls_off[tid] = before + incl - n;
       if (tid == kTailClasses - 1) {
         a.ws_ctrl[kCtrlEntries] = before + incl;

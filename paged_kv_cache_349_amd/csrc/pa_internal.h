@@ -40,7 +40,7 @@ struct DecodeParams {
                               //  first block: the sequence's shared-prefix blocks, else 0)
   int2* ws_split;             // [S] (sequence, partitions) of sequences spanning several:
                               //  up to kMergeShort partitions from the front, more from the back
-  int32_t* ws_ctrl;           // [kCtrlSize] written by the planner
+  int32_t* ws_ctrl;           // [kCtrlSize] control words (planner, kernels)
   // Shared prefixes (num_groups == 0: none).  Sequences group_starts[g] ..
   // group_starts[g+1]-1 share their first prefix_blocks[g] table entries.
   const int32_t* group_starts;  // [num_groups + 1]
@@ -75,9 +75,9 @@ constexpr int kCtrlAbort = 20;
 // the mark is present and clears this word.
 constexpr int kCtrlAbortPlanned = 21;
 constexpr int32_t kAbortMark = 0x5a17ab07;
-// Claim counters of the matrix-core kernel's work list, one per pool
-// (workgroups b with b % kClaimPools == x claim from pool x), each in a
-// 128-byte line of its own; zeroed by the planner.
+// Claim counters of the matrix-core kernel's work list, one per pool, each
+// in a 128-byte line of its own; zeroed by the planner (the self-planning
+// kernel claims nothing).
 constexpr int kClaimPools = 32;
 constexpr int kClaimStride = 32;
 constexpr int kCtrlClaims = 32;
