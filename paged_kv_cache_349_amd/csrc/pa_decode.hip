@@ -1943,8 +1943,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
       ap[j] = p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4)
                               : f4{0.f, 0.f, 0.f, 0.f};
     }
-    float m = kNegInf;
-    for (int p = tid; p < nparts; p += kMergeThreads) m = fmaxf(m, ml[(prow + p) * G + gq].x);
+    // The thread's first (m, l) pair stays in registers for the sum below
+    // (no second read after the barrier); further ones (more partitions than
+    // threads) are read again.
+    const float2 first = tid < nparts ? ml[(prow + tid) * G + gq] : make_float2(kNegInf, 0.f);
+    float m = first.x;
+    for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads)
+      m = fmaxf(m, ml[(prow + p) * G + gq].x);
     m = wave_max_f(m);
     if (lane == 0) head_max[wave] = m;
     __syncthreads();
@@ -1953,7 +1958,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     for (int v = 0; v < kMergeWaves; ++v) M = fmaxf(M, head_max[v]);
     float l = 0.f;
     if (M != kNegInf) {
-      for (int p = tid; p < nparts; p += kMergeThreads) {
+      if (first.x != kNegInf) l += first.y * exp2_fast(first.x - M);
+      for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads) {
         const float2 v = ml[(prow + p) * G + gq];
         if (v.x != kNegInf) l += v.y * exp2_fast(v.x - M);
       }
