@@ -1891,12 +1891,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
       float2 mlp[kMergeShort];
       f4 ap[kMergeShort];
       float M = kNegInf;
+      // Only the unit's partitions are read (a guarded load, not a clamped
+      // address the compiler may load from unconditionally): a unit of 2
+      // partitions reads 2 states, not kMergeShort.
 #pragma unroll
       for (int j = 0; j < kMergeShort; ++j) {
-        const int64_t row = (prow + min(j, nparts - 1)) * G + g;
-        mlp[j] = j < nparts ? ml[row] : make_float2(kNegInf, 0.f);
-        ap[j] = j < nparts ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4)
-                           : f4{0.f, 0.f, 0.f, 0.f};
+        mlp[j] = make_float2(kNegInf, 0.f);
+        ap[j] = f4{0.f, 0.f, 0.f, 0.f};
+        if (j < nparts) {
+          const int64_t row = (prow + j) * G + g;
+          mlp[j] = ml[row];
+          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + d4 * 4);
+        }
       }
 #pragma unroll
       for (int j = 0; j < kMergeShort; ++j) M = fmaxf(M, mlp[j].x);
@@ -1938,10 +1944,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
     f4 ap[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const int64_t row = (prow + max(min(p_lo + j, p_hi - 1), 0)) * G + gq;
-      mp[j] = p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
-      ap[j] = p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4)
-                              : f4{0.f, 0.f, 0.f, 0.f};
+      mp[j] = kNegInf;
+      ap[j] = f4{0.f, 0.f, 0.f, 0.f};
+      if (p_lo + j < p_hi) {
+        const int64_t row = (prow + p_lo + j) * G + gq;
+        mp[j] = a.ws_ml[row * 2];
+        ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
+      }
     }
     // The thread's first (m, l) pair stays in registers for the sum below
     // (no second read after the barrier); further ones (more partitions than
@@ -1974,13 +1983,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
       for (int p0 = p_lo + kMergeBatch; p0 < p_hi; p0 += kMergeBatch) {
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j) {
-          const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + gq;
-          mp[j] = a.ws_ml[row * 2];
-          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
+          mp[j] = kNegInf;
+          ap[j] = f4{0.f, 0.f, 0.f, 0.f};
+          if (p0 + j < p_hi) {
+            const int64_t row = (prow + p0 + j) * G + gq;
+            mp[j] = a.ws_ml[row * 2];
+            ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
+          }
         }
 #pragma unroll
         for (int j = 0; j < kMergeBatch; ++j)
-          if (p0 + j < p_hi && mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
+          if (mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
       }
     }
     partial[tid] = val;
