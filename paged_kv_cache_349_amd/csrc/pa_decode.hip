@@ -1882,9 +1882,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
   const int n_short = a.ws_ctrl[kCtrlSplits] * Hkv;
   const int n_long = a.ws_ctrl[kCtrlLongSplits] * Hkv;
 
+  // A short unit's list entry is read before the unit counts are known (its
+  // index is clamped into the list, and the entry is used only for units
+  // below the count), so the first entry and the counts arrive in one memory
+  // round trip.  (The same for the long units below measured slower on the
+  // skewed long-context workload, 6.56 vs 6.10 us.)
   if (r < R) {
-    for (int u = blockIdx.x + r * gridDim.x; u < n_short; u += gridDim.x * R) {
-      const int2 e = a.ws_split[u / Hkv];
+    int u = blockIdx.x + r * gridDim.x;
+    int2 e_next = a.ws_split[min(u / Hkv, S - 1)];
+    for (; u < n_short; u += (int)gridDim.x * R) {
+      const int2 e = e_next;
+      e_next = a.ws_split[min((u + (int)gridDim.x * R) / Hkv, S - 1)];
       const int h = u % Hkv;
       const int s = e.x, nparts = e.y;
       const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;   // partition 0's row
