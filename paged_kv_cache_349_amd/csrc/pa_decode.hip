@@ -314,12 +314,14 @@ struct LanePlan {
   int n_full, n_tail;
 };
 
+// `len`: context_lens[lane] as read (lanes past the batch: anything).
 template <int BS>
-__device__ __forceinline__ LanePlan lane_plan(const DecodeParams& a) {
+__device__ __forceinline__ LanePlan lane_plan(const DecodeParams& a, int len) {
   LanePlan q;
   const int lane = threadIdx.x & 63;
   const bool live = lane < a.num_seqs;
-  q.L = live ? clamp_len(a, lane, BS) : 0;
+  const int Lmax = a.max_blocks * BS;
+  q.L = live ? (len < 0 ? 0 : (len > Lmax ? Lmax : len)) : 0;
   q.nblk = (q.L + BS - 1) / BS;
   q.pb = choose_part_blocks(a, wave_sum(q.nblk), a.decode_grid, a.balance);
   q.nfull = live ? (q.nblk == 0 ? 1 : q.nblk / q.pb) : 0;
@@ -373,7 +375,7 @@ __device__ __forceinline__ void write_split_list(const DecodeParams& a, const La
 template <int BS>
 __device__ __forceinline__ void plan_small(const DecodeParams& a) {
   const int lane = threadIdx.x & 63;
-  const LanePlan q = lane_plan<BS>(a);
+  const LanePlan q = lane_plan<BS>(a, lane < a.num_seqs ? a.lens[lane] : 0);
   const int pbp = choose_part_blocks(a, 0, a.decode_grid / 2, 0);
   // A sequence's first kDirectItems full partitions are listed by its lane,
   // any further ones by all lanes together.
@@ -1230,7 +1232,24 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   const PA_CONST int32_t* items = as_const((const int32_t*)a.ws_items);   // int4 entries
   const PA_CONST int32_t* tables = as_const(a.tables);
   LanePlan lp{};
-  if constexpr (PLAN) lp = lane_plan<BS>(a);
+  // Self-planning kernel: the block tables are pulled into the caches while
+  // the plan is computed, so that an item's first block id is a cache hit
+  // rather than one more HBM round trip after the lengths.  Each lane reads
+  // one word of one table line (every wave, so no branch makes the wait for
+  // the lengths also wait for this load); the workgroups of one XCD
+  // (dispatched round-robin: workgroup b on XCD b % 8) cover every line of
+  // the first 2 MB of tables.  The word is used only after the stream (an
+  // empty asm statement), so no wait is added for it.
+  int warm = 0;
+  if constexpr (PLAN) {
+    const int len = lane < a.num_seqs ? a.lens[lane] : 0;   // issued first: waited for first
+    const int64_t lines = ((int64_t)a.num_seqs * a.max_blocks + 31) / 32;
+    const int64_t per_xcd = (NG + 7 - (bid & 7)) >> 3;
+    const int64_t line =
+        min((int64_t)(bid >> 3) + (int64_t)(lane + 64 * w) * per_xcd, lines - 1);
+    warm = a.tables[line * 32];
+    lp = lane_plan<BS>(a, len);
+  }
   const int total = PLAN ? (lp.n_full + lp.n_tail) * Hkv : ctrl[kCtrlEntries] * Hkv;
   const int pb = PLAN ? lp.pb : ctrl[kCtrlPartBlocks];
   const int pbp = PLAN ? 1 : ctrl[kCtrlPrefixPart];
@@ -1704,6 +1723,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 
   while (step(t0, has0, t1, has1) && step(t1, has1, t0, has0)) {
   }
+  if constexpr (PLAN) asm volatile("" ::"v"(warm));
 }
 
 // ---------------------------------------------------------------------------
