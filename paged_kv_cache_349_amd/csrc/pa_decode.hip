@@ -68,6 +68,7 @@
 
 #include <climits>
 #include <cstdlib>
+#include <type_traits>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -954,6 +955,49 @@ __device__ __forceinline__ void load_half(Tile<D, 16>& t, __amdgpu_buffer_rsrc_t
                                                     0, kStreamLoad));
 }
 
+// fp32 KV on the matrix cores (v_mfma_f32_16x16x4_f32, fp32 products and
+// sums), per 16-token position:
+//   S^T[16 tokens x 16 heads] = sum over D/4 products of K[16 x 4] Q^T[4 x 16]
+//   O^T[16 d x 16 heads]     += V^T[16 d x 4] P^T[4 x 16], 4 per 16 features
+// Token t's K row is held by lanes t, t+16, t+32, t+48, lane quarter q with
+// D/4 contiguous features from q*D/4 (four 16-byte loads per 64 features);
+// the query the same way per head.  Product j takes feature q*D/4 + j in
+// quarter q: a fixed permutation of the sum over features.  V is read as in
+// the bf16 kernel, lane (feature d, quarter q) with tokens 4q .. 4q+3 of
+// feature d, and PV product c pairs token 4q + c with its weight, which the
+// score layout already puts in that lane, so P never leaves registers.
+template <int D>
+struct TileF32 {
+  f32x4 k[D / 16];   // features (D/4)*quad + 4c .. +3 of token (lane % 16)
+  f32x4 v[D / 16];   // tokens 4*quad .. +3 of feature 16i + (lane % 16)
+};
+
+template <int D>
+__device__ __forceinline__ LaneOff lane_offsets_f32(int lane, int group) {
+  const uint32_t row = lane & 15, quad = lane >> 4;
+  LaneOff o;
+  o.k = (row * D + quad * (D / 4)) * 4;
+  o.v = (row * 16 + quad * 4) * 4;
+  o.q = (int)row < group ? (row * D + quad * (D / 4)) * 4 : (uint32_t)group * D * 4;
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ void load_half_f32(TileF32<D>& t, __amdgpu_buffer_rsrc_t kr,
+                                              __amdgpu_buffer_rsrc_t vr, const LaneOff& o,
+                                              int half) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    t.k[c] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + half * 16 * D * 4 + c * 16, 0,
+                                                     kStreamLoad));
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i)
+    t.v[i] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, o.v + (half * 16 * D + i * 16 * 16) * 4,
+                                                     0, kStreamLoad));
+}
+
 // Read-only views through the constant address space: uniform reads of
 // them become scalar loads, which are counted apart from the vector loads
 // that stream the K/V tiles, so waiting for a block id never drains the tile
@@ -1215,8 +1259,15 @@ struct Desc {
 // the workspace has to be zeroed first); workgroup 0 writes the split list
 // for merge_splits.  A wait that gives up is recorded in its own word, which
 // merge_splits turns into the call's abort word.
-template <int D, int BS, int W, bool PREFIX, bool TABLE = true, bool PLAN = false>
-__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
+// E: KV element, uint16_t (bf16 bits) or float.
+template <typename E, int D, int BS, int W, bool PREFIX, bool TABLE, bool PLAN>
+__device__ __forceinline__ void decode_mfma_body(const DecodeParams& a) {
+  constexpr bool F32 = sizeof(E) == 4;
+  static_assert(!(F32 && PREFIX), "shared prefixes run on bf16 KV only");
+  using TileT = typename std::conditional<F32, TileF32<D>, Tile<D, 16>>::type;
+  struct QB { bf16x8 v[D / 32]; };
+  struct QF { f32x4 v[D / 16]; };
+  using QT = typename std::conditional<F32, QF, QB>::type;
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1465,8 +1516,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   const char* kbase = (const char*)a.k_cache;
   const char* vbase = (const char*)a.v_cache;
   const char* qbase = (const char*)a.q;
-  const uint32_t tile_bytes = (uint32_t)BS * D * 2;
-  const LaneOff lo = lane_offsets<D, BS>(lane, G);
+  const uint32_t tile_bytes = (uint32_t)BS * D * sizeof(E);
+  LaneOff lo;
+  if constexpr (F32) lo = lane_offsets_f32<D>(lane, G);
+  else lo = lane_offsets<D, BS>(lane, G);
 
   // Loads of one position into a buffer.  `has` says whether the position
   // holds a block of the wave; a block id outside the pool counts as none,
@@ -1475,7 +1528,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   // reloading it (2 KB per wave and position, from the cache) made the whole
   // decode call 4.4% slower (219.5 against 209.8 us on the large-batch
   // workload), the extra cache traffic competing with the tile stream.
-  auto load_pos = [&](Tile<D, 16>& t, const Desc& d, int k, bool& has) {
+  auto load_pos = [&](TileT& t, const Desc& d, int k, bool& has) {
     const int q = d.wr + k * W;
     const int kk = q / kHalves, half = q - kk * kHalves;
     int id = 0;
@@ -1487,15 +1540,24 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     has = d.valid && k < d.nmine && (unsigned)id < (unsigned)a.num_blocks;
     const int64_t off = has ? ((int64_t)id * Hkv + d.h) * tile_bytes : 0;
     const uint32_t nb = has ? tile_bytes : 0;
-    load_half<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo, half);
+    if constexpr (F32)
+      load_half_f32<D>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo, half);
+    else
+      load_half<D, BS>(t, buffer_of(kbase + off, nb), buffer_of(vbase + off, nb), lo, half);
   };
-  auto load_q = [&](bf16x8* q, const Desc& d) {
+  auto load_q = [&](QT& q, const Desc& d) {
     const __amdgpu_buffer_rsrc_t qr = buffer_of(
-        qbase + ((int64_t)(d.valid ? d.s : 0) * a.num_heads + d.h * G) * D * 2,
-        d.valid ? (uint32_t)G * D * 2 : 0);
+        qbase + ((int64_t)(d.valid ? d.s : 0) * a.num_heads + d.h * G) * D * sizeof(E),
+        d.valid ? (uint32_t)(G * D * sizeof(E)) : 0);
+    if constexpr (F32) {
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      q[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, lo.q + c * 64, 0, 0));
+      for (int c = 0; c < D / 16; ++c)
+        q.v[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, lo.q + c * 16, 0, 0));
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        q.v[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, lo.q + c * 64, 0, 0));
+    }
   };
 
   float m = kNegInf, lsum = 0.f;
@@ -1505,26 +1567,35 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 
   // One position: scores, online-softmax update, weighted values.  Positions
   // >= live are masked; live <= 0 masks the whole block.
-  auto compute = [&](Tile<D, 16>& t, const bf16x8* qop, int live) {
-    f32x4 sc[Tile<D, 16>::SB];
+  auto compute = [&](TileT& t, const QT& q, int live) {
+    f32x4 sc;
+    if constexpr (F32) {
+      // Four independent chains of products, added at the end (a single
+      // chain of D/4 dependent products would serialise on its latency).
+      f32x4 part[4];
 #pragma unroll
-    for (int sb = 0; sb < Tile<D, 16>::SB; ++sb) {
-      sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < 4; ++u) part[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          part[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[c][u], q.v[c][u], part[u], 0, 0, 0);
+      sc = (part[0] + part[1]) + (part[2] + part[3]);
+    } else {
+      sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
-        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[sb][c], qop[c], sc[sb], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[0][c], q.v[c], sc, 0, 0, 0);
     }
     // Scale into base-2 units, mask dead positions (select, never multiply:
     // the tail of the last block may hold anything), block max per head.
     float mx = kNegInf;
 #pragma unroll
-    for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float x = sb * 16 + quad * 4 + rr < live ? sc[sb][rr] * a.scale_log2 : kNegInf;
-        sc[sb][rr] = x;
-        mx = fmaxf(mx, x);
-      }
+    for (int rr = 0; rr < 4; ++rr) {
+      const float x = quad * 4 + rr < live ? sc[rr] * a.scale_log2 : kNegInf;
+      sc[rr] = x;
+      mx = fmaxf(mx, x);
+    }
     mx = rows_max(mx);
     const float mnew = fmaxf(m, mx);
     // Exponent reference: the running max, or 0 while every position seen so
@@ -1532,43 +1603,62 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
     const float mref = mnew == kNegInf ? 0.f : mnew;
     const float alpha = exp2_fast(m - mref);       // 0 on the first live block
     m = mnew;
-    i16x4 pw[Tile<D, 16>::SB], pl[Tile<D, 16>::SB];
-    float psum = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const SplitWeight sw = split_weight(exp2_fast(sc[sb][rr] - mref));
-        pw[sb][rr] = sw.hi;
-        pl[sb][rr] = sw.lo;
-        psum += sw.sum;
-      }
-    lsum = lsum * alpha + psum;
     // Rescale every time (alpha is exactly 1 while a head's running max holds,
     // and multiplying by 1 changes nothing): skipping it behind a wave-uniform
     // test made the compiler copy the 32 accumulator registers at every
-    // position, which cost as much as the multiplies.
+    // position, which cost as much as the multiplies.  A partly dead block
+    // has V of its dead positions zeroed (their weight is 0, but 0 * NaN is
+    // NaN).
+    float psum = 0.f;
+    if constexpr (F32) {
+      f32x4 p;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
-    // Partly dead block: zero V of dead positions (their weight is 0, but
-    // 0 * NaN is NaN).
-    if (live < 16) {
+      for (int rr = 0; rr < 4; ++rr) {
+        p[rr] = exp2_fast(sc[rr] - mref);
+        psum += p[rr];
+      }
+      lsum = lsum * alpha + psum;
 #pragma unroll
-      for (int sb = 0; sb < Tile<D, 16>::SB; ++sb)
+      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+      if (live < 16) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const bool dead = sb * 16 + quad * 4 + rr >= live;
+          const bool dead = quad * 4 + rr >= live;
 #pragma unroll
-          for (int i = 0; i < D / 16; ++i) t.v[sb][i][rr] = dead ? (short)0 : t.v[sb][i][rr];
+          for (int i = 0; i < D / 16; ++i) t.v[i][rr] = dead ? 0.f : t.v[i][rr];
         }
-    }
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-#pragma unroll
-      for (int sb = 0; sb < Tile<D, 16>::SB; ++sb) {
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pw[sb], acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[sb][i], pl[sb], acc[i], 0, 0, 0);
       }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[i][c], p[c], acc[i], 0, 0, 0);
+    } else {
+      i16x4 pw, pl;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const SplitWeight sw = split_weight(exp2_fast(sc[rr] - mref));
+        pw[rr] = sw.hi;
+        pl[rr] = sw.lo;
+        psum += sw.sum;
+      }
+      lsum = lsum * alpha + psum;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
+      if (live < 16) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const bool dead = quad * 4 + rr >= live;
+#pragma unroll
+          for (int i = 0; i < D / 16; ++i) t.v[0][i][rr] = dead ? (short)0 : t.v[0][i][rr];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[0][i], pw, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[0][i], pl, acc[i], 0, 0, 0);
+      }
+    }
   };
 
   // End of an item, without a barrier: the wave stores its state in the
@@ -1678,10 +1768,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   };
 
   // The stream.  Position (cur, k); its buffer was loaded one step earlier.
-  Tile<D, 16> t0, t1;
+  TileT t0, t1;
   // The query of round r's item is in set r & 1: loaded with the item's first
   // position (one position ahead), used until the item ends.
-  bf16x8 qa[D / 32], qb[D / 32];
+  QT qa, qb;
   bool has0 = false, has1 = false;
   int k = 0;
   load_q(qa, cur);
@@ -1689,7 +1779,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
 
   // One step: load the next position into (tn, qn), compute (tc, qc).
   // Returns false when the stream has ended.
-  auto step = [&](Tile<D, 16>& tc, bool hc, Tile<D, 16>& tn, bool& hn) -> bool {
+  auto step = [&](TileT& tc, bool hc, TileT& tn, bool& hn) -> bool {
     const bool last = k + 1 >= cur.npos;
     if (last && !have_nxt) {
       nxt = desc(r + 1);
@@ -1724,6 +1814,18 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
   while (step(t0, has0, t1, has1) && step(t1, has1, t0, has0)) {
   }
   if constexpr (PLAN) asm volatile("" ::"v"(warm));
+}
+
+template <int D, int BS, int W, bool PREFIX, bool TABLE = true, bool PLAN = false>
+__global__ __launch_bounds__(64 * W) void decode_mfma_bf16(DecodeParams a) {
+  decode_mfma_body<uint16_t, D, BS, W, PREFIX, TABLE, PLAN>(a);
+}
+
+// fp32 KV: the same work list, stream and merge, with fp32 matrix-core
+// products (no shared-prefix phase; no packed-pool diagnostic).
+template <int D, int BS, int W, bool PLAN = false>
+__global__ __launch_bounds__(64 * W) void decode_mfma_f32(DecodeParams a) {
+  decode_mfma_body<float, D, BS, W, false, true, PLAN>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -2116,10 +2218,15 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   // A batch the one-wave planner would plan, decoded without a slot write in
   // the same call, is planned inside the attention kernel instead: one
   // launch less (merge_splits, which then always follows, reports its waits).
-  const bool plan_inside = type == KvType::BF16 && !vector_alu && !prefix && !packed && !write &&
-                           small_plan(p) && p.num_parts_max > 1;
+  const bool plan_inside = !vector_alu && !prefix && !packed && !write && small_plan(p) &&
+                           p.num_parts_max > 1;
   p.inline_plan = plan_inside ? 1 : 0;
-  if (type == KvType::BF16 && !vector_alu) {
+  const bool f32_mfma = type == KvType::F32 && !vector_alu;
+  if (f32_mfma) {
+    kernel = plan_inside ? (const void*)decode_mfma_f32<D, BS, kWaves, true>
+                         : (const void*)decode_mfma_f32<D, BS, kWaves, false>;
+    smem = smem_bytes<D>(p0.group, false, BS, p.lds_slots, p.lds_records);
+  } else if (type == KvType::BF16 && !vector_alu) {
     kernel = prefix ? (const void*)decode_mfma_bf16<D, BS, kWaves, true>
              : packed ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, false>
              : plan_inside ? (const void*)decode_mfma_bf16<D, BS, kWaves, false, true, true>
@@ -2172,7 +2279,13 @@ hipError_t launch_decode_shape(const DecodeParams& p0, KvType type, bool vector_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
-  if (type == KvType::BF16 && !vector_alu && prefix)
+  if (f32_mfma && plan_inside)
+    hipLaunchKernelGGL((decode_mfma_f32<D, BS, kWaves, true>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else if (f32_mfma)
+    hipLaunchKernelGGL((decode_mfma_f32<D, BS, kWaves, false>), dim3(p.decode_grid),
+                       dim3(threads), smem, stream, p);
+  else if (type == KvType::BF16 && !vector_alu && prefix)
     hipLaunchKernelGGL((decode_mfma_bf16<D, BS, kWaves, true>), dim3(p.decode_grid),
                        dim3(threads), smem, stream, p);
   else if (type == KvType::BF16 && !vector_alu && packed)

@@ -142,6 +142,20 @@ def test_vector_alu_kernel_bf16(partition_tokens):
     _bars(float(np.abs(out - ref).max()), "bf16")
 
 
+@pytest.mark.parametrize("vector_alu", [False, True])
+@pytest.mark.parametrize("partition_tokens", [0, 16, 64])
+def test_f32_matrix_core_and_vector_alu(partition_tokens, vector_alu):
+    """fp32 KV runs the matrix-core kernel (fp32 products); the vector-ALU
+    kernel stays available for it behind the same switch.  Both against the
+    oracle at the fp32 bar."""
+    lens = [1, 17, 100, 300, 1000, 33]
+    w = _custom(lens, 16, 4, 128, 16, "f32", seed=9)
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, 16, "f32")
+    out = _run(w, vector_alu=vector_alu, partition_tokens=partition_tokens).out.cpu().numpy()
+    _bars(float(np.abs(out - ref).max()), "f32")
+
+
 def _custom(lens, Hq, Hkv, D, bs, dtype, seed=0, poison="nan", num_blocks=None):
     rng = np.random.default_rng(seed)
     return wl.build_workload("custom", rng, kv_dtype=dtype, context_lens=lens, num_heads=Hq,
