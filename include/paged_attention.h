@@ -202,8 +202,9 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
  * pa_decode with the context split made explicit, for tests and tuning.
  * partition_tokens: tokens handled by one workgroup (a multiple of
  * block_size, or 0 for the library's choice).  flags: PA_FLAG_VECTOR_ALU
- * selects the plain vector-ALU kernel also for bf16 (by default bf16 uses the
- * matrix-core kernel).  PA_FLAG_PACKED_POOL is a diagnostic for a pool that
+ * selects the plain vector-ALU kernel (by default both bf16 and fp32 KV use
+ * the matrix-core kernel: bf16 products with fp32 sums, or fp32 products).
+ * PA_FLAG_PACKED_POOL is a diagnostic for a pool that
  * holds each sequence's blocks consecutively: block j of sequence s is taken
  * to be block_tables[s, 0] + j, and only the first entry of each row is read
  * (bf16 matrix-core kernel only; else PA_ERR_UNSUPPORTED).  On such a pool it
