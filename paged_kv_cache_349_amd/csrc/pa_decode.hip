@@ -42,7 +42,7 @@
 // `out` directly; otherwise the item stores its partition state in the
 // workspace for merge_splits.
 //
-// Matrix-core kernel (bf16).  For each 16-token sub-block:
+// Matrix-core kernel, bf16 KV.  For each 16-token sub-block:
 //   S^T[16 tokens x 16 heads] = K[16 x D] * Q^T[D x 16]      (v_mfma_f32_16x16x32_bf16)
 //   O^T[16 d x 16 heads]     += V^T[16 d x 16] * P^T[16 x 16] (v_mfma_f32_16x16x16_bf16)
 // The G query heads of a KV group fill the 16-wide head dimension (padded
@@ -58,7 +58,10 @@
 // bf16(P - hi) (see split_weight), so the weights keep about 16 bits; the
 // softmax denominator sums the same hi + lo.
 //
-// Vector-ALU kernel (fp32, and bf16 on request): the same items and merge;
+// fp32 KV runs the same matrix-core kernel with fp32 products
+// (v_mfma_f32_16x16x4_f32; see TileF32).
+//
+// Vector-ALU kernel (either dtype, on request): the same items and merge;
 // scores by lanes over tokens, weighted values by lanes over features.
 //
 // Shared prefixes (pa_decode_shared_prefix): the matrix-core kernel first
