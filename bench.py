@@ -125,6 +125,18 @@ def bench_ceilings(w, d, dev, stream, kern_mean_us):
     }
 
 
+def copy_calibration(dev):
+    """One plain 1 GiB device-to-device copy: a known byte count for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run of the same job."""
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: one 1 GiB device copy done")
+
+
 def bench_shared_prefix(args, dev, stream):
     """Parallel sampling: 16 prompts of 2048 tokens, 8 samples each with private
     tails of 1..513 tokens (bf16, 32/8 heads, D 128, bs 16).  pa_decode reads
@@ -528,6 +540,8 @@ def main() -> int:
         [int(c) for c in args.configs.split(",") if c.strip()]
     if args.configs_only:
         res = bench_configs(args, dev, torch.cuda.current_stream(dev), which)
+        if args.copy_calibration:
+            copy_calibration(dev)
         print(json.dumps({"configs": res}), flush=True)
         return 0
 
@@ -751,11 +765,7 @@ def main() -> int:
         del dc
 
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy calibration: one 1 GiB device copy done")
+        copy_calibration(dev)
 
     if not args.no_ceilings:
         result["ceilings"] = bench_ceilings(w, d, dev, stream, kern_mean)
