@@ -1970,7 +1970,8 @@ __global__ __launch_bounds__(64 * W) void decode_valu(DecodeParams a) {
 //   thread-strided partitions; rows of threads take contiguous runs of
 //   partitions of one column for the weighted sum, whose terms do not depend
 //   on one another, and the rows' partial sums are added in row order.  A
-//   row's first kMergeBatch partitions are loaded before the reductions.
+//   row's first partitions (8, 16 or kMergeBatch, as many as its run needs)
+//   are loaded before the reductions.
 //   (One workgroup per unit, all heads together: the skewed long-context
 //   workload's merge of a 128-partition sequence took 7.7 us per call.)
 // Every order depends only on the partition count, so results are
@@ -1981,9 +1982,99 @@ constexpr int kMergeBatch = 32;
 constexpr int kMergeGrid = 256;
 static_assert(kMergeShort <= kMergeBatch, "a short unit's partitions are loaded in one batch");
 
+typedef float merge_f4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// One query head of a long unit (sequence s, KV head h, query head gq of the
+// group, nparts partition states).  The head's maximum and sum come first
+// (thread t takes partitions t, t + threads, ...); then rows of D/4 threads
+// take contiguous runs of partitions of one column each, and the rows'
+// partial sums are added in row order.  A row's first B partitions are
+// loaded before the reductions: clamped addresses, so the compiler issues
+// every load of the batch at once (guarded loads measured 1 us slower on a
+// cold long unit), with B no larger than a row's run needs, since each
+// clamped slot past the run is one more load instruction through the
+// texture-address unit.
+template <int D, int B>
+__device__ __forceinline__ void merge_long_head(const DecodeParams& a, int s, int h, int gq,
+                                                int nparts, float* head_max, float* head_sum,
+                                                merge_f4* partial) {
+  typedef merge_f4 f4;
+  constexpr int kCols4 = D / 4;
+  constexpr int kRowsH = kMergeThreads / kCols4;
+  const int G = a.group, Hkv = a.num_kv_heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rh = tid / kCols4, ch = tid - rh * kCols4;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
+  const int p_lo = (int)((int64_t)nparts * rh / kRowsH);
+  const int p_hi = (int)((int64_t)nparts * (rh + 1) / kRowsH);
+  // This row's first batch of weighted sums, in flight during the reductions.
+  float mp[B];
+  f4 ap[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int64_t row = (prow + max(min(p_lo + j, p_hi - 1), 0)) * G + gq;
+    mp[j] = p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
+    ap[j] = p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4)
+                            : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  // The thread's first (m, l) pair stays in registers for the sum below
+  // (no second read after the barrier); further ones (more partitions than
+  // threads) are read again.
+  const float2 first = tid < nparts ? ml[(prow + tid) * G + gq] : make_float2(kNegInf, 0.f);
+  float m = first.x;
+  for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads)
+    m = fmaxf(m, ml[(prow + p) * G + gq].x);
+  m = wave_max_f(m);
+  if (lane == 0) head_max[wave] = m;
+  __syncthreads();
+  float M = kNegInf;
+#pragma unroll
+  for (int v = 0; v < kMergeWaves; ++v) M = fmaxf(M, head_max[v]);
+  float l = 0.f;
+  if (M != kNegInf) {
+    if (first.x != kNegInf) l += first.y * exp2_fast(first.x - M);
+    for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads) {
+      const float2 v = ml[(prow + p) * G + gq];
+      if (v.x != kNegInf) l += v.y * exp2_fast(v.x - M);
+    }
+  }
+  l = wave_sum_f(l);
+  if (lane == 0) head_sum[wave] = l;
+  f4 val = {0.f, 0.f, 0.f, 0.f};
+  if (M != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
+    for (int p0 = p_lo + B; p0 < p_hi; p0 += B) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + gq;
+        mp[j] = a.ws_ml[row * 2];
+        ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        if (p0 + j < p_hi && mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
+    }
+  }
+  partial[tid] = val;
+  __syncthreads();
+  if (tid < kCols4) {
+    f4 sum = partial[tid];
+    for (int rr = 1; rr < kRowsH; ++rr) sum += partial[rr * kCols4 + tid];
+    float lam = 0.f;
+#pragma unroll
+    for (int v = 0; v < kMergeWaves; ++v) lam += head_sum[v];
+    *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + gq) * D + tid * 4) =
+        lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();   // head_max, head_sum and partial are reused by the next unit
+}
+
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
-  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+  typedef merge_f4 f4;
   constexpr int kCols4 = D / 4;
   __shared__ float head_max[kMergeWaves], head_sum[kMergeWaves];
   __shared__ f4 partial[kMergeThreads];
@@ -2057,85 +2148,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits(DecodeParams a) {
 
   // Long units, one query head per workgroup (so a long sequence's partition
   // states are read by G workgroups at once, not one): unit u is (split
-  // sequence u / (Hkv * G), KV head, query head u % G).  The head's maximum
-  // and sum come first (thread t takes partitions t, t + threads, ...), then
-  // rows of kCols4 threads take contiguous runs of partitions of one column
-  // each, and the rows' partial sums are added in row order.
+  // sequence u / (Hkv * G), KV head, query head u % G).  The batch a row of
+  // threads loads at once is sized to the row's run of partitions (8, 16 or
+  // 32), uniform over the workgroup.
   constexpr int kRowsH = kMergeThreads / kCols4;
-  const int rh = tid / kCols4, ch = tid - rh * kCols4;
   for (int u = gridDim.x - 1 - blockIdx.x; u < n_long * G; u += gridDim.x) {
     const int uh = u / G;                      // (split sequence, KV head)
     const int gq = (int)(u - uh * G);
     const int2 e = a.ws_split[S - 1 - uh / Hkv];
     const int h = uh % Hkv;
-    const int s = e.x, nparts = e.y;
-    const int64_t prow = ((int64_t)s * Hkv + h) * a.num_parts_max;
-    const int p_lo = (int)((int64_t)nparts * rh / kRowsH);
-    const int p_hi = (int)((int64_t)nparts * (rh + 1) / kRowsH);
-    // This row's first batch of weighted sums, in flight during the reductions.
-    float mp[kMergeBatch];
-    f4 ap[kMergeBatch];
-    // Clamped addresses, so the compiler issues every load of the batch at
-    // once (guarded loads measured 1 us slower on a cold long unit).
-#pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      const int64_t row = (prow + max(min(p_lo + j, p_hi - 1), 0)) * G + gq;
-      mp[j] = p_lo + j < p_hi ? a.ws_ml[row * 2] : kNegInf;
-      ap[j] = p_lo + j < p_hi ? *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4)
-                              : f4{0.f, 0.f, 0.f, 0.f};
-    }
-    // The thread's first (m, l) pair stays in registers for the sum below
-    // (no second read after the barrier); further ones (more partitions than
-    // threads) are read again.
-    const float2 first = tid < nparts ? ml[(prow + tid) * G + gq] : make_float2(kNegInf, 0.f);
-    float m = first.x;
-    for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads)
-      m = fmaxf(m, ml[(prow + p) * G + gq].x);
-    m = wave_max_f(m);
-    if (lane == 0) head_max[wave] = m;
-    __syncthreads();
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < kMergeWaves; ++v) M = fmaxf(M, head_max[v]);
-    float l = 0.f;
-    if (M != kNegInf) {
-      if (first.x != kNegInf) l += first.y * exp2_fast(first.x - M);
-      for (int p = tid + kMergeThreads; p < nparts; p += kMergeThreads) {
-        const float2 v = ml[(prow + p) * G + gq];
-        if (v.x != kNegInf) l += v.y * exp2_fast(v.x - M);
-      }
-    }
-    l = wave_sum_f(l);
-    if (lane == 0) head_sum[wave] = l;
-    f4 val = {0.f, 0.f, 0.f, 0.f};
-    if (M != kNegInf) {
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j)
-        if (mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
-      for (int p0 = p_lo + kMergeBatch; p0 < p_hi; p0 += kMergeBatch) {
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) {
-          const int64_t row = (prow + min(p0 + j, p_hi - 1)) * G + gq;
-          mp[j] = a.ws_ml[row * 2];
-          ap[j] = *reinterpret_cast<const f4*>(a.ws_acc + row * D + ch * 4);
-        }
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j)
-          if (p0 + j < p_hi && mp[j] != kNegInf) val += ap[j] * exp2_fast(mp[j] - M);
-      }
-    }
-    partial[tid] = val;
-    __syncthreads();
-    if (tid < kCols4) {
-      f4 sum = partial[tid];
-      for (int rr = 1; rr < kRowsH; ++rr) sum += partial[rr * kCols4 + tid];
-      float lam = 0.f;
-#pragma unroll
-      for (int v = 0; v < kMergeWaves; ++v) lam += head_sum[v];
-      *reinterpret_cast<f4*>(a.out + ((int64_t)s * a.num_heads + h * G + gq) * D + tid * 4) =
-          lam > 0.f ? sum / lam : f4{0.f, 0.f, 0.f, 0.f};
-    }
-    __syncthreads();   // head_max, head_sum and partial are reused by the next unit
+    const int span = (e.y + kRowsH - 1) / kRowsH;   // partitions per row, at most
+    if (span <= 8)
+      merge_long_head<D, 8>(a, e.x, h, gq, e.y, head_max, head_sum, partial);
+    else if (span <= 16)
+      merge_long_head<D, 16>(a, e.x, h, gq, e.y, head_max, head_sum, partial);
+    else
+      merge_long_head<D, kMergeBatch>(a, e.x, h, gq, e.y, head_max, head_sum, partial);
   }
 }
 
