@@ -135,6 +135,36 @@ def test_partition_sizes_long_context(partition_tokens):
     _bars(err, "bf16")
 
 
+# (head_dim, dtype, long context, partition tokens): a sequence with more than
+# 16 partitions is merged by rows of D/4 threads (16 rows at D 128, 32 at D
+# 64), each loading its run of partitions in batches of 8, 16 or 32; these
+# lengths give runs of at most 8, of 9..16, of 17..32 and of more than 32
+# (several batches) at both head sizes.
+LONG_MERGE_CASES = [(128, "bf16", 1800, 16), (128, "bf16", 4000, 16), (128, "f32", 4000, 16),
+                    (128, "bf16", 8000, 16), (128, "bf16", 12000, 16),
+                    (64, "bf16", 3000, 16), (64, "bf16", 8000, 16), (64, "f32", 8000, 16),
+                    (64, "bf16", 16000, 16), (64, "bf16", 20000, 16)]
+
+
+@pytest.mark.parametrize("case", LONG_MERGE_CASES, ids=lambda c: "D%d-%s-L%d-pt%d" % c)
+def test_long_merge_batches(case):
+    """Long contexts split into 112..1250 partitions beside short sequences
+    (which take the one-thread-per-column merge) agree with the oracle."""
+    D, dt, L, pt = case
+    lens = [L, 40, 0, 700, L // 2 + 3]
+    w = _custom(lens, 32, 8, D, 16, dt, seed=L + D)
+    k_ref, v_ref = oracle.write_kv(w.k_cache, w.v_cache, w.k_new, w.v_new, w.slot_mapping, 16)
+    ref = oracle.decode(w.q, k_ref, v_ref, w.block_tables, w.context_lens, w.scale, 16, dt)
+    parts = -(-L // pt)
+    rows = 512 // (D // 4)
+    _say(f"D={D} {dt} L={L} pt={pt}: {parts} partitions, runs of up to {-(-parts // rows)} per row")
+    out = _run(w, partition_tokens=pt).out.cpu().numpy()
+    err = float(np.abs(out - ref).max())
+    _say(f"  max-abs err {err:.3e}")
+    assert np.all(out[2] == 0.0)
+    _bars(err, dt)
+
+
 @pytest.mark.parametrize("partition_tokens", [0, 16, 64])
 def test_vector_alu_kernel_bf16(partition_tokens):
     w, _, _, ref = _case(cfg=2, num_seqs=6)
